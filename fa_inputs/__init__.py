@@ -1,0 +1,219 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module holds no attention arithmetic. It draws random numbers and rounds
+them to the storage dtypes, and it is the one piece of code that both sides of a
+parity check share: the fp64 CPU oracle gets the exact values of the stored
+tensors, the GPU library gets the stored tensors themselves.
+
+Random numbers
+    SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+    generators", OOPSLA 2014).  Output k (k = 0, 1, ...) of the stream with seed s
+    is mix(s + (k+1)*0x9E3779B97F4A7C15 mod 2^64), which makes the generator
+    counter-based and lets numpy draw any slice of the stream directly.
+    A uniform is (x >> 11) * 2^-53 in [0, 1).  Normals come in pairs by the
+    Box-Muller transform (Box and Muller, 1958) from uniforms (2p, 2p+1):
+    r = sqrt(-2 ln(1 - u0)), n0 = r cos(2 pi u1), n1 = r sin(2 pi u1).
+
+Fill order
+    Q, then K, then V, each in row-major [B, H, N, d] order; every tensor starts on
+    a fresh normal pair.  When a per-head query bias is requested, Hq uniforms
+    follow V and beta_h = 2 u_h is added to every element of Q[:, h].  Values are
+    multiplied (then biased) in fp64 and rounded once, fp64 -> storage dtype,
+    round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "splitmix64", "Stream", "round_to_dtype", "to_storage", "storage_to_f64",
+    "AttentionInputs", "make_inputs", "WORKLOADS", "workload",
+]
+
+_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_MIX1 = np.uint64(0xBF58476D1CE4E5B9)
+_MIX2 = np.uint64(0x94D049BB133111EB)
+_CHUNK = 1 << 22  # normal pairs generated per numpy pass (bounds temporaries)
+
+
+def splitmix64(seed: int, start: int, count: int) -> np.ndarray:
+    """Outputs start .. start+count-1 of the SplitMix64 stream seeded with `seed`."""
+    with np.errstate(over="ignore"):
+        k = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + k * _GAMMA
+        z = (z ^ (z >> np.uint64(30))) * _MIX1
+        z = (z ^ (z >> np.uint64(27))) * _MIX2
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def _uniform53(z: np.ndarray) -> np.ndarray:
+    return (z >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
+
+
+class Stream:
+    """A cursor over one seeded SplitMix64 stream, counted in uniforms."""
+
+    def __init__(self, seed: int):
+        self.seed = int(seed)
+        self.pos = 0
+
+    def uniforms(self, count: int) -> np.ndarray:
+        u = _uniform53(splitmix64(self.seed, self.pos, count))
+        self.pos += count
+        return u
+
+    def normals(self, count: int) -> np.ndarray:
+        """`count` N(0,1) draws; consumes 2*ceil(count/2) uniforms."""
+        pairs = (count + 1) // 2
+        out = np.empty(2 * pairs, dtype=np.float64)
+        for p0 in range(0, pairs, _CHUNK):
+            np_ = min(_CHUNK, pairs - p0)
+            u = self.uniforms(2 * np_)
+            r = np.sqrt(-2.0 * np.log1p(-u[0::2]))
+            t = (2.0 * math.pi) * u[1::2]
+            out[2 * p0:2 * (p0 + np_):2] = r * np.cos(t)
+            out[2 * p0 + 1:2 * (p0 + np_):2] = r * np.sin(t)
+        return out[:count]
+
+
+# (precision p in bits incl. the implicit one, minimum normal exponent, largest finite)
+_FORMATS = {
+    "bf16": (8, -126, float.fromhex("0x1.fep127")),
+    "f16": (11, -14, 65504.0),
+}
+
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values once, to nearest-even, onto the grid of `dtype`.
+
+    Returns fp64 values that the dtype represents exactly (so the result is the
+    exact value of the stored tensor).  Subnormals are kept; overflow goes to inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x.copy()
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    p, emin, big = _FORMATS[dtype]
+    _, e = np.frexp(x)  # |x| in [2^(e-1), 2^e)
+    sh = np.maximum(e.astype(np.int64) - p, emin - p + 1)
+    r = np.ldexp(np.round(np.ldexp(x, -sh)), sh)  # np.round: ties to even
+    r = np.where(np.abs(r) > big, np.copysign(np.inf, x), r)
+    return np.where(np.isnan(x), x, r)
+
+
+def to_storage(x_rounded: np.ndarray, dtype: str) -> np.ndarray:
+    """Pack values already on the dtype grid into their storage array.
+
+    bf16 is returned as int16 bit patterns (numpy has no bf16), f16 as float16,
+    f32 as float32.
+    """
+    if dtype == "f64":
+        return np.ascontiguousarray(x_rounded, dtype=np.float64)
+    if dtype == "f32":
+        return x_rounded.astype(np.float32)
+    if dtype == "f16":
+        return x_rounded.astype(np.float16)
+    if dtype == "bf16":
+        bits = x_rounded.astype(np.float32).view(np.uint32) >> np.uint32(16)
+        return bits.astype(np.uint16).view(np.int16)
+    raise ValueError(dtype)
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of a storage array produced by `to_storage`."""
+    if dtype == "bf16":
+        u32 = a.view(np.uint16).astype(np.uint32) << np.uint32(16)
+        return u32.view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+@dataclass
+class AttentionInputs:
+    """One seeded problem: storage arrays plus everything needed to describe it."""
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float          # an fp32 value, held as a Python float
+    seed: int
+    q: np.ndarray         # storage arrays, shapes [B,Hq,N,d] / [B,Hkv,N,d]
+    k: np.ndarray
+    v: np.ndarray
+    recipe: str = ""
+    extra: dict = field(default_factory=dict)
+
+    def f64(self, name: str) -> np.ndarray:
+        return storage_to_f64(getattr(self, name), self.dtype)
+
+    @property
+    def flops(self) -> float:
+        """4*B*Hq*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to fp32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def make_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str,
+                causal: bool, scale: float | None = None, mult: float = 1.0,
+                q_head_bias: bool = False, recipe: str = "") -> AttentionInputs:
+    """Draw Q, K, V for one problem in the module's fill order and round them."""
+    st = Stream(seed)
+    shp_q, shp_kv = (B, Hq, N, d), (B, Hkv, N, d)
+    q = st.normals(int(np.prod(shp_q))).reshape(shp_q)
+    k = st.normals(int(np.prod(shp_kv))).reshape(shp_kv)
+    v = st.normals(int(np.prod(shp_kv))).reshape(shp_kv)
+    extra = {}
+    if mult != 1.0:
+        q *= mult
+        k *= mult
+        v *= mult
+    if q_head_bias:
+        beta = 2.0 * st.uniforms(Hq)
+        q += beta[None, :, None, None]
+        extra["q_head_bias"] = beta
+    out = []
+    for x in (q, k, v):
+        out.append(to_storage(round_to_dtype(x, dtype), dtype))
+        del x
+    return AttentionInputs(B, Hq, Hkv, N, d, dtype, bool(causal),
+                           default_scale(d) if scale is None else float(np.float32(scale)),
+                           int(seed), out[0], out[1], out[2], recipe, extra)
+
+
+# The six measured workloads.  Shapes follow the pages' layers: a 4096-token
+# Llama-7B layer (32 heads of 128), BERT-large at sequence 512, 32/8 grouped-query
+# heads, and long contexts with inputs scaled by 3 to exercise the rescaling.
+WORKLOADS = {
+    "f32_h1_n128_d64": dict(seed=1001, B=1, Hq=1, Hkv=1, N=128, d=64, dtype="f32",
+                            causal=False, tuning=(32, 32)),
+    "bf16_h32_n4096_d128_causal": dict(seed=1002, B=1, Hq=32, Hkv=32, N=4096, d=128,
+                                       dtype="bf16", causal=True),
+    "f16_b16_h16_n512_d64_qbias": dict(seed=1003, B=16, Hq=16, Hkv=16, N=512, d=64,
+                                       dtype="f16", causal=False, q_head_bias=True),
+    "bf16_gqa_b4_hq32_hkv8_n8192_d128_causal": dict(seed=1004, B=4, Hq=32, Hkv=8,
+                                                    N=8192, d=128, dtype="bf16",
+                                                    causal=True),
+    "bf16_h16_n32768_d128_causal_x3": dict(seed=1005, B=1, Hq=16, Hkv=16, N=32768,
+                                           d=128, dtype="bf16", causal=True, mult=3.0),
+    "bf16_h8_n8192_d256_causal_x3": dict(seed=1006, B=1, Hq=8, Hkv=8, N=8192, d=256,
+                                         dtype="bf16", causal=True, mult=3.0),
+}
+
+
+def workload(name: str) -> AttentionInputs:
+    """Generate one of the named workloads (may take seconds for the large ones)."""
+    w = dict(WORKLOADS[name])
+    w.pop("tuning", None)
+    return make_inputs(recipe=name, **w)

@@ -1,0 +1,255 @@
+/*
+ * attention_oracle.c -- plain, slow fp64 CPU oracle of the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or loads
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * do.  It shares no code, header or constant with the GPU path.
+ *
+ * What it computes is the plain definition, written out:
+ *
+ *   Attention(Q,K,V) = softmax(Q K^T * scale) V
+ *       -- "FlashAttention (VI)", section "Vấn đề của cơ chế attention tiêu chuẩn",
+ *          equation Attention (scale = 1/sqrt(d_k) there; here the caller passes it).
+ *
+ * following the standard path of "MCU 上 Transformer 模型的 Flash Attention 实现…"
+ * §一 (Q x K^T gives an [N,N] score matrix, which then multiplies V) and the
+ * two-pass softmax of its §二, first paragraph (pass 1: the row maximum; pass 2:
+ * the sum of exp(x - max)).  Scores are materialised for a block of query rows
+ * at a time, each row holding all N columns; rows are independent, so the result
+ * does not depend on the block size.
+ *
+ * Readings where the pages are silent:
+ *   - causal: key j is visible to query i iff j <= i ("FlashAttention 在昇腾 NPU 上…",
+ *     pitfall 1: a generation model must not see the future);
+ *   - grouped-query heads: query head h reads key/value head h / (Hq/Hkv), so each
+ *     key/value head serves Hq/Hkv consecutive query heads ("深度探索Flash-Attention中
+ *     GQA性能调优技术解析", GQA mechanism);
+ *   - lse[b,h,i] = m_i + ln(l_i), natural log, in units of scaled scores.
+ *
+ * Layouts: q, o are [B,Hq,N,d]; k, v are [B,Hkv,N,d]; lse is [B,Hq,N]; all fp64,
+ * contiguous, d innermost.  With a row list, o and lse hold only those rows, in
+ * list order: o is [B,Hq,nrows,d], lse is [B,Hq,nrows].
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+typedef struct {
+    const double *q, *k, *v;
+    double *o, *lse, *probs;
+    int64_t B, Hq, Hkv, N, d;
+    int causal;
+    double scale;
+    const int64_t *rows;   /* query rows computed for every (b, h); NULL = all   */
+    int64_t nrows;         /* length of the row list (N when rows == NULL)       */
+    int64_t chunk;         /* rows per work unit                                 */
+    int64_t units_per_bh;
+    int64_t nunits;
+    int64_t next;
+    int failed;
+    pthread_mutex_t mu;
+} oracle_job;
+
+static int64_t row_index(const oracle_job *J, int64_t r)
+{
+    return J->rows ? J->rows[r] : r;
+}
+
+/* One work unit: query rows [r0, r1) of the row list, for one (b, h). */
+static void run_unit(const oracle_job *J, int64_t unit, double *S)
+{
+    const int64_t bh = unit / J->units_per_bh;
+    const int64_t b = bh / J->Hq, h = bh % J->Hq;
+    const int64_t group = J->Hq / J->Hkv;
+    const int64_t hk = h / group;
+    const int64_t N = J->N, d = J->d;
+    const int64_t r0 = (unit % J->units_per_bh) * J->chunk;
+    const int64_t r1 = (r0 + J->chunk < J->nrows) ? r0 + J->chunk : J->nrows;
+
+    const double *qh = J->q + (b * J->Hq + h) * N * d;
+    const double *kh = J->k + (b * J->Hkv + hk) * N * d;
+    const double *vh = J->v + (b * J->Hkv + hk) * N * d;
+
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t i = row_index(J, r);
+        const int64_t jend = J->causal ? i + 1 : N;   /* visible keys: j < jend */
+        double *s = S + (r - r0) * N;
+        const double *qi = qh + i * d;
+
+        /* Scores s_ij = scale * sum_t q_it k_jt, the full row materialised. */
+        for (int64_t j = 0; j < jend; ++j) {
+            const double *kj = kh + j * d;
+            double acc = 0.0;
+            for (int64_t t = 0; t < d; ++t)
+                acc += qi[t] * kj[t];
+            s[j] = J->scale * acc;
+        }
+
+        /* Pass 1: the row maximum over the visible keys. */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < jend; ++j)
+            if (s[j] > m)
+                m = s[j];
+
+        /* Pass 2: e_ij = exp(s_ij - m_i), l_i = sum_j e_ij; then P_ij = e_ij / l_i. */
+        double l = 0.0;
+        for (int64_t j = 0; j < jend; ++j) {
+            s[j] = exp(s[j] - m);
+            l += s[j];
+        }
+        for (int64_t j = 0; j < jend; ++j)
+            s[j] = s[j] / l;
+
+        /* O_i = sum_j P_ij v_j. */
+        double *oi = J->o ? J->o + (bh * J->nrows + r) * d : NULL;
+        if (oi) {
+            for (int64_t t = 0; t < d; ++t)
+                oi[t] = 0.0;
+            for (int64_t j = 0; j < jend; ++j) {
+                const double *vj = vh + j * d;
+                for (int64_t t = 0; t < d; ++t)
+                    oi[t] += s[j] * vj[t];
+            }
+        }
+        if (J->lse)
+            J->lse[bh * J->nrows + r] = m + log(l);
+        if (J->probs) {
+            double *pr = J->probs + (bh * J->nrows + r) * N;
+            for (int64_t j = 0; j < N; ++j)
+                pr[j] = j < jend ? s[j] : 0.0;
+        }
+    }
+}
+
+static void *worker(void *arg)
+{
+    oracle_job *J = (oracle_job *)arg;
+    double *S = (double *)malloc((size_t)(J->chunk * J->N) * sizeof(double));
+    if (!S) {
+        pthread_mutex_lock(&J->mu);
+        J->failed = 1;
+        pthread_mutex_unlock(&J->mu);
+        return NULL;
+    }
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int64_t u = J->failed ? J->nunits : J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->nunits)
+            break;
+        run_unit(J, u, S);
+    }
+    free(S);
+    return NULL;
+}
+
+static int run_job(oracle_job *J, int threads)
+{
+    /* Keep each thread's score block at or below 64 MB. */
+    int64_t chunk = (64LL << 20) / (8 * J->N);
+    if (chunk < 1)
+        chunk = 1;
+    if (chunk > J->nrows)
+        chunk = J->nrows;
+    J->chunk = chunk;
+    J->units_per_bh = (J->nrows + chunk - 1) / chunk;
+    J->nunits = J->B * J->Hq * J->units_per_bh;
+    J->next = 0;
+    J->failed = 0;
+    pthread_mutex_init(&J->mu, NULL);
+
+    if (threads <= 0)
+        threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (threads < 1)
+        threads = 1;
+    if (threads > J->nunits)
+        threads = (int)J->nunits;
+
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!tid)
+        return -3;
+    int started = 0;
+    for (int t = 1; t < threads; ++t) {
+        if (pthread_create(&tid[t], NULL, worker, J) != 0)
+            break;
+        ++started;
+    }
+    worker(J);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    pthread_mutex_destroy(&J->mu);
+    return J->failed ? -3 : 0;
+}
+
+static int check_args(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                      const int64_t *rows, int64_t nrows)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv != 0)
+        return -2;
+    if (rows) {
+        if (nrows < 1)
+            return -2;
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return -2;
+    }
+    return 0;
+}
+
+/*
+ * o and lse for every (b, h) and every query row in `rows` (all N rows when rows
+ * is NULL).  Either output may be NULL.  Returns 0, -1 on a NULL input, -2 on a bad
+ * shape or row index, -3 when memory or threads cannot be had.  threads <= 0 uses
+ * every online CPU.
+ */
+int oracle_attention_fwd(const double *q, const double *k, const double *v,
+                         double *o, double *lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                         int causal, double scale,
+                         const int64_t *rows, int64_t nrows, int threads)
+{
+    if (!q || !k || !v)
+        return -1;
+    if (!rows)
+        nrows = N;
+    int rc = check_args(B, Hq, Hkv, N, d, rows, nrows);
+    if (rc)
+        return rc;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.probs = NULL;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.causal = causal != 0;
+    J.scale = scale;
+    J.rows = rows;
+    J.nrows = nrows;
+    return run_job(&J, threads);
+}
+
+/*
+ * The softmax matrix P itself, [B,Hq,N,N] (zeros where a key is masked), for small
+ * problems.  Same arithmetic as oracle_attention_fwd.
+ */
+int oracle_attention_probs(const double *q, const double *k, double *probs,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                           int causal, double scale)
+{
+    if (!q || !k || !probs)
+        return -1;
+    int rc = check_args(B, Hq, Hkv, N, d, NULL, N);
+    if (rc)
+        return rc;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = k; J.o = NULL; J.lse = NULL; J.probs = probs;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.causal = causal != 0;
+    J.scale = scale;
+    J.rows = NULL;
+    J.nrows = N;
+    return run_job(&J, 1);
+}

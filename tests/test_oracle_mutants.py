@@ -1,0 +1,74 @@
+"""Planted mistakes in copies of the oracle sources must fail a pin.
+
+Each mutant edits one or two expressions of a copy of the C sources in a
+temporary directory, builds it with gcc and runs the pins against it.  The real
+sources are never touched.  A mutant that no pin catches fails this test.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+ORACLE = "attention_oracle.c"
+BLOCKED = "blocked_reference.c"
+
+# (id, file, [(original, replacement), ...])
+MUTANTS = [
+    ("causal_strict", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i : N")]),
+    ("causal_leak", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i + 2 : N")]),
+    ("gqa_modulo", ORACLE, [("const int64_t hk = h / group;", "const int64_t hk = h % J->Hkv;")]),
+    ("exp_sign", ORACLE, [("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);")]),
+    ("no_scale", ORACLE, [("s[j] = J->scale * acc;", "s[j] = acc;")]),
+    ("no_normalise", ORACLE, [("s[j] = s[j] / l;", "s[j] = s[j];")]),
+    ("drop_first_value", ORACLE, [("for (int64_t j = 0; j < jend; ++j) {\n                const double *vj",
+                                   "for (int64_t j = 1; j < jend; ++j) {\n                const double *vj")]),
+    ("value_row_i", ORACLE, [("const double *vj = vh + j * d;", "const double *vj = vh + i * d;")]),
+    ("transposed_scores", ORACLE, [("const double *qi = qh + i * d;", "const double *qi = kh + i * d;"),
+                                   ("const double *kj = kh + j * d;", "const double *kj = qh + j * d;")]),
+    ("lse_without_max", ORACLE, [("= m + log(l);", "= log(l);")]),
+    ("dot_skips_last", ORACLE, [("for (int64_t t = 0; t < d; ++t)\n                acc += qi[t] * kj[t];",
+                                 "for (int64_t t = 0; t + 1 < d; ++t)\n                acc += qi[t] * kj[t];")]),
+    ("key_head_not_query_head", ORACLE, [("const double *kh = J->k + (b * J->Hkv + hk) * N * d;",
+                                          "const double *kh = J->k + (b * J->Hkv + h % J->Hkv) * N * d;")]),
+    ("blocked_no_rescale_l", BLOCKED, [("l[i] = a_old * l[i] + a_blk * lt;", "l[i] = l[i] + a_blk * lt;")]),
+    ("blocked_no_rescale_o", BLOCKED, [("acc[i * d + t] = a_old * acc[i * d + t] + a_blk * pv[t];",
+                                        "acc[i * d + t] = acc[i * d + t] + a_blk * pv[t];")]),
+    ("blocked_alpha_sign", BLOCKED, [("const double a_old = exp(m[i] - mn);", "const double a_old = exp(mn - m[i]);")]),
+    ("blocked_causal_strict", BLOCKED, [("causal ? ((i + 1 < j1) ? i + 1 : j1) : j1", "causal ? ((i < j1) ? i : j1) : j1")]),
+    ("blocked_local_max_ignored", BLOCKED, [("const double p = exp(sblk[j - j0] - mt);",
+                                             "const double p = exp(sblk[j - j0] - mn_unused);"),
+                                            ("double lt = 0.0;", "double lt = 0.0; const double mn_unused = (m[i] > mt) ? m[i] : mt;")]),
+]
+
+
+def _quick_oracle_pins(lib):
+    P.pin_brute_force(lib, quick=True)
+    P.pin_torch_sdpa(lib)
+    P.pin_closed_forms(lib)
+    P.pin_invariants(lib)
+
+
+def _build_mutant(tmp_path, fname, edits):
+    srcs = []
+    for s in oracle.SOURCES:
+        dst = tmp_path / s
+        shutil.copy(os.path.join(oracle.HERE, s), dst)
+        srcs.append(str(dst))
+    path = tmp_path / fname
+    text = path.read_text()
+    for old, new in edits:
+        assert text.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+        text = text.replace(old, new)
+    path.write_text(text)
+    return oracle.load(oracle.build(str(tmp_path / "libmutant.so"), tuple(srcs)))
+
+
+@pytest.mark.parametrize("mid,fname,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, mid, fname, edits):
+    lib = _build_mutant(tmp_path, fname, edits)
+    pins = _quick_oracle_pins if fname == ORACLE else (lambda L: P.pin_blocked_agrees(L, quick=True))
+    with pytest.raises(AssertionError):
+        pins(lib)
