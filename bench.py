@@ -1,0 +1,224 @@
+"""Benchmark of the FlashAttention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --profile-run      # a few launches + a calibration copy, for rocprofv3
+
+A step is one pass of the whole hot path -- one fused forward kernel -- over one
+batch of seeded synthetic inputs already resident in device memory.  The default
+workload is the causal bf16 layer B=1, H=32, N=4096, d=128.  Prints one JSON line.
+
+value       = algorithmic FLOPs (4*B*Hq*N^2*d, halved when causal) * K / wall time of
+              the K timed steps, bracketed by device synchronisation.
+roofline    = the kernel's own rate: FLOPs per launch / average launch duration from
+              HIP events recorded on the launch stream around the timed region, against
+              the 2.5 PFLOP/s dense bf16 MFMA peak.  traffic = HBM bytes per launch from
+              rocprofv3 FETCH_SIZE / WRITE_SIZE counters, calibrated on a copy of known
+              size (read from profiles/, null when the kernel sources changed since).
+cpu_baseline = the fp64 CPU oracle, as it stands, on a bounded sample of query rows of
+              the same workload, on this host's cores, in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (causal, d=128, N=4096)"
+DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp")
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha") != kernel_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def device_inputs(x, dev):
+    import torch
+    out = []
+    for n in "qkv":
+        a = getattr(x, n)
+        t = torch.from_numpy(a).view(torch.bfloat16) if x.dtype == "bf16" else torch.from_numpy(a)
+        out.append(t.to(dev))
+    return out
+
+
+def cpu_baseline(x, budget_s: float = 15.0) -> dict:
+    """Time the oracle on a bounded sample of the workload and scale to TFLOP/s.
+
+    The sample is whole query heads (b = 0, heads 0, 1, ...) when one head takes
+    less than the budget, otherwise every k-th query row of head 0.  FLOPs are
+    counted as for the GPU: 4*d per visible (query, key) pair.
+    """
+    import numpy as np
+
+    import oracle
+    from fa_inputs import storage_to_f64
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    G = x.Hq // x.Hkv
+
+    def f64(name, h0, h1):
+        return storage_to_f64(np.ascontiguousarray(getattr(x, name)[0:1, h0:h1]), x.dtype)
+
+    def row_flops(rows):
+        keys = (rows + 1) if x.causal else np.full(len(rows), x.N)
+        return float(4.0 * x.d * keys.sum())
+
+    # Calibrate on a few rows spread over the causal range of head 0.
+    q, k, v = f64("q", 0, 1), f64("k", 0, 1), f64("v", 0, 1)
+    rows = np.arange(x.N - 1, -1, -31, dtype=np.int64)[::-1].copy()
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, x.causal, x.scale, rows=rows, threads=threads)
+    rate = row_flops(rows) / max(time.perf_counter() - t0, 1e-3)
+    head_flops = row_flops(np.arange(x.N))
+    n_heads = int(rate * budget_s // head_flops)
+
+    if n_heads >= 1:
+        n_heads = min(x.Hq, max(G, n_heads // G * G))
+        q, k, v = f64("q", 0, n_heads), f64("k", 0, n_heads // G), f64("v", 0, n_heads // G)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, x.causal, x.scale, threads=threads)
+        dt = time.perf_counter() - t0
+        flops = head_flops * n_heads
+        sample = f"all {x.N} query rows of heads 0..{n_heads - 1} (batch 0) of {x.recipe}"
+    else:
+        every = int(math.ceil(head_flops / (rate * budget_s)))
+        rows = np.arange(0, x.N, every, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, x.causal, x.scale, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        flops = row_flops(rows)
+        sample = f"every {every}th query row of head (0,0) of {x.recipe}"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads"}
+
+
+def run(args) -> dict:
+    import torch
+
+    import fa_inputs as G
+    import io_aware_attention_amd as F
+
+    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
+    torch.cuda.set_device(dev)
+    x = G.workload(args.workload)
+    tuning = G.WORKLOADS[args.workload].get("tuning")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.dtype]
+    plan = F.plan(x.B, x.Hq, x.Hkv, x.N, x.d, x.causal, tdt, tuning=tuning, scale=x.scale)
+    q, k, v = device_inputs(x, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((x.B, x.Hq, x.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        F.fwd(q, k, v, causal=x.causal, scale=x.scale, o=o, lse=lse, tuning=tuning, stream=stream)
+
+    if args.profile_run:
+        for _ in range(3):
+            step()
+        # Calibration copy of known size for the HBM byte counters.
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"profile_run": args.workload, "copy_bytes": src.numel() * 4}), flush=True)
+        return {}
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = e0.elapsed_time(e1) / args.steps
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output")
+
+    flops = x.flops
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[x.dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": x.B, "Hq": x.Hq, "Hkv": x.Hkv, "N": x.N,
+                   "d": x.d, "causal": x.causal, "scale": x.scale, "seed": x.seed,
+                   "tile": [plan.br, plan.bc], "waves": plan.waves, "grid": plan.grid},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": load_traffic(args.workload),
+                     "kernel_us": round(kernel_ms * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    return line
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-run", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the forward pass of one device's share is "
+              f"the whole hot path here; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    line = run(args)
+    if line:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

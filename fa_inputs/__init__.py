@@ -24,6 +24,8 @@ Fill order
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -36,7 +38,19 @@ __all__ = [
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _MIX1 = np.uint64(0xBF58476D1CE4E5B9)
 _MIX2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22  # normal pairs generated per numpy pass (bounds temporaries)
+_CHUNK = 1 << 19  # normal pairs per numpy pass (bounds temporaries, feeds threads)
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(n: int, step: int, fn) -> None:
+    """fn(start, stop) over [0, n) in chunks, on a thread pool (numpy drops the GIL)."""
+    starts = range(0, n, step)
+    if len(starts) <= 1:
+        for a in starts:
+            fn(a, min(n, a + step))
+        return
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(lambda a: fn(a, min(n, a + step)), starts))
 
 
 def splitmix64(seed: int, start: int, count: int) -> np.ndarray:
@@ -70,13 +84,17 @@ class Stream:
         """`count` N(0,1) draws; consumes 2*ceil(count/2) uniforms."""
         pairs = (count + 1) // 2
         out = np.empty(2 * pairs, dtype=np.float64)
-        for p0 in range(0, pairs, _CHUNK):
-            np_ = min(_CHUNK, pairs - p0)
-            u = self.uniforms(2 * np_)
+        base = self.pos
+
+        def fill(p0, p1):
+            u = _uniform53(splitmix64(self.seed, base + 2 * p0, 2 * (p1 - p0)))
             r = np.sqrt(-2.0 * np.log1p(-u[0::2]))
             t = (2.0 * math.pi) * u[1::2]
-            out[2 * p0:2 * (p0 + np_):2] = r * np.cos(t)
-            out[2 * p0 + 1:2 * (p0 + np_):2] = r * np.sin(t)
+            out[2 * p0:2 * p1:2] = r * np.cos(t)
+            out[2 * p0 + 1:2 * p1:2] = r * np.sin(t)
+
+        _chunked(pairs, _CHUNK, fill)
+        self.pos += 2 * pairs
         return out[:count]
 
 
@@ -98,12 +116,46 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
         return x.copy()
     if dtype == "f32":
         return x.astype(np.float32).astype(np.float64)
+    if dtype == "bf16" and x.size > 4096:
+        return _round_bf16_fast(x)
+    return _round_general(x, dtype)
+
+
+def _round_general(x: np.ndarray, dtype: str) -> np.ndarray:
     p, emin, big = _FORMATS[dtype]
     _, e = np.frexp(x)  # |x| in [2^(e-1), 2^e)
     sh = np.maximum(e.astype(np.int64) - p, emin - p + 1)
     r = np.ldexp(np.round(np.ldexp(x, -sh)), sh)  # np.round: ties to even
     r = np.where(np.abs(r) > big, np.copysign(np.inf, x), r)
     return np.where(np.isnan(x), x, r)
+
+
+def _round_bf16_fast(x: np.ndarray) -> np.ndarray:
+    """Same result as _round_general(x, "bf16"), by integer rounding of the fp64 bits.
+
+    In bf16's normal range, keeping the top 7 of fp64's 52 fraction bits with
+    round-half-even is: add 2^44 - 1 plus the lowest kept bit, clear the 45 low bits
+    (a carry correctly bumps the exponent).  Values outside that range go through
+    the general path.
+    """
+    flat = np.ascontiguousarray(x).reshape(-1)
+    out = np.empty_like(flat)
+    lo, hi = 2.0 ** -126, float.fromhex("0x1.fep127")
+    keep = np.uint64(~((1 << 45) - 1) & 0xFFFFFFFFFFFFFFFF)
+
+    def work(a, b):
+        xs = flat[a:b]
+        bits = xs.view(np.uint64)
+        lsb = (bits >> np.uint64(45)) & np.uint64(1)
+        r = ((bits + (np.uint64((1 << 44) - 1) + lsb)) & keep).view(np.float64)
+        ax = np.abs(xs)
+        odd = ~((ax >= lo) & (ax <= hi))
+        if odd.any():
+            r = np.where(odd, _round_general(xs, "bf16"), r)
+        out[a:b] = r
+
+    _chunked(flat.size, 1 << 20, work)
+    return out.reshape(x.shape)
 
 
 def to_storage(x_rounded: np.ndarray, dtype: str) -> np.ndarray:

@@ -1,0 +1,127 @@
+/*
+ * fa355.h -- FlashAttention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes exact scaled-dot-product attention
+ *
+ *     O = softmax(Q K^T * scale) V,      lse = logsumexp of each scaled score row
+ *
+ * ("FlashAttention (VI)", section "Vấn đề của cơ chế attention tiêu chuẩn", eq.
+ * Attention) in a single fused kernel: Q is split into row tiles, K and V stream
+ * through on-chip memory in row blocks, and the running row maximum, row sum and
+ * rescaled output stay on chip through the online-softmax recurrence ("MCU 上
+ * Transformer 模型的 Flash Attention 实现…", §二, flowchart and merge equations;
+ * "FlashAttention (VI)", sections on tiling, online softmax and kernel fusion).
+ * The N x N score matrix never reaches device memory, and the library allocates
+ * nothing: memory use is the caller's O(N) tensors only ("FlashAttention 在昇腾 NPU
+ * 上是怎么省显存的？", tiling section: only two rows of softmax statistics are kept).
+ *
+ * Tensor layout follows the pages' user API, [batch, heads, seq_len, head_dim]
+ * ("FlashAttention 在昇腾 NPU 上…", section on running the operator):
+ *   q, o : [B, Hq,  N, d]    contiguous, d innermost
+ *   k, v : [B, Hkv, N, d]    contiguous, d innermost
+ *   lse  : [B, Hq,  N]       fp32, natural log, in units of scaled scores
+ * Grouped-query attention is expressed by the K/V head count alone (same page,
+ * pitfall 4; "深度探索Flash-Attention中GQA性能调优技术解析", GQA mechanism): query head
+ * h reads K/V head h / (Hq / Hkv), i.e. Hq/Hkv consecutive query heads share one.
+ * Causal masking lets query row i see key rows j <= i (same Ascend page, pitfall 1).
+ *
+ * Ownership: the caller allocates and frees every buffer; pointers are device
+ * pointers.  Asynchrony: a successful call enqueues exactly one kernel on `stream`
+ * (NULL = the null stream) and returns; results are valid once the stream has
+ * reached that point.  Calls are reentrant and thread-safe; the library keeps no
+ * mutable state.  Errors: arguments are validated before any HIP call; on any
+ * error the call returns a negative fa355_status and leaves o and lse untouched.
+ * There is no silent fallback: an unsupported head dimension, dtype or tiling is an
+ * error, never a slower path (contrast "FlashAttention…昇腾…" page 2, pitfall).
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA355_F32 = 0,
+    FA355_F16 = 1,
+    FA355_BF16 = 2
+} fa355_dtype;
+
+typedef enum {
+    FA355_OK = 0,
+    FA355_ERR_NULL = -1,        /* q, k, v or o is NULL                                   */
+    FA355_ERR_SHAPE = -2,       /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow  */
+    FA355_ERR_UNSUPPORTED = -3, /* head dim, dtype pair or tiling not built               */
+    FA355_ERR_ALIGN = -4,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte      */
+    FA355_ERR_ARG = -5,         /* non-finite scale; o or lse overlapping another buffer  */
+    FA355_ERR_HIP = -6          /* the HIP launch reported an error                        */
+} fa355_status;
+
+/* Tile sizes: br = query rows per workgroup, bc = key/value rows per step.
+ * {0, 0} (or a NULL pointer) selects the built-in choice for the shape. */
+typedef struct {
+    int br;
+    int bc;
+} fa355_tuning;
+
+/* What a call would launch; filled by fa_fwd_check. */
+typedef struct {
+    int br;            /* query rows per workgroup                     */
+    int bc;            /* key/value rows per step                      */
+    int waves;         /* 64-lane wavefronts per workgroup             */
+    int grid;          /* workgroups launched                          */
+    int lds_bytes;     /* LDS per workgroup                            */
+} fa355_plan;
+
+/*
+ * Forward attention, output in the input dtype.
+ *   q, k, v   device pointers, layouts above, element type `dtype`
+ *   o         device pointer [B,Hq,N,d] of `dtype`; written
+ *   lse       device pointer [B,Hq,N] fp32, or NULL to skip it
+ *   B, Hq, Hkv, N, d   sizes; d in {64, 128, 256} for F16/BF16, d = 64 for F32
+ *   causal    nonzero: query i sees keys j <= i
+ *   scale     multiplies Q K^T; any finite value (1/sqrt(d) is the usual one)
+ *   stream    HIP stream to enqueue on
+ * Returns FA355_OK or a negative fa355_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           fa355_dtype dtype, hipStream_t stream);
+
+/*
+ * As fa_fwd, plus:
+ *   o_dtype   the output element type: in_dtype, or FA355_F32 for F16/BF16 inputs
+ *             (identical arithmetic; only the final store differs)
+ *   tuning    NULL or {0,0} for the default tiles, else one of the built tilings
+ *             (br, bc) in {(128,64), (64,64), (128,32), (256,64)} for F16/BF16 and
+ *             {(32,32), (64,32), (128,32)} for F32
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+              fa355_dtype in_dtype, fa355_dtype o_dtype,
+              const fa355_tuning *tuning, hipStream_t stream);
+
+/*
+ * Validation only: runs every check fa_fwd_ex runs, makes no HIP call and
+ * launches nothing.  On FA355_OK and a non-NULL `plan`, fills in the launch the
+ * call would make.  Pointers are only compared and tested for alignment, never
+ * dereferenced, so host addresses may be passed.
+ */
+int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
+                 const float *lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                 float scale, fa355_dtype in_dtype, fa355_dtype o_dtype,
+                 const fa355_tuning *tuning, fa355_plan *plan);
+
+/* A static, human-readable name for a status code ("unknown status" otherwise). */
+const char *fa_status_str(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

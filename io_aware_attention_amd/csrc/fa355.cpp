@@ -1,0 +1,234 @@
+// fa355.cpp -- the C ABI of libfa355: argument validation, variant choice, launch.
+//
+// Validation runs completely before any HIP call, so every error leaves the
+// outputs untouched and can be exercised on a machine without a GPU.  A valid
+// call enqueues exactly one kernel and allocates nothing.
+#include "fa355.h"
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "fa_args.hpp"
+
+namespace {
+
+using LaunchFn = hipError_t (*)(const fa355::FwdArgs &, hipStream_t);
+
+struct Variant {
+    int dtype;      // fa355_dtype of the inputs
+    int d;
+    int bc;
+    int waves;
+    bool causal;
+    bool out_f32;
+    int lds;
+    LaunchFn fn;
+};
+
+#define FA355_DT_BF16 FA355_BF16
+#define FA355_DT_F16 FA355_F16
+#define FA355_ROW(T, D, BC, W, C, O) \
+    {FA355_DT_##T, D, BC, W, C, O, 8 * (BC) * (D), &fa355::launch_fwd<fa355::T, D, BC, W, C, O>},
+#define FA355_ROW_F32(W, C) \
+    {FA355_F32, 64, 32, W, C, false, (32 * 65 + 32 * 64) * 4, &fa355::launch_fwd_f32<W, C>},
+
+const Variant kVariants[] = {
+    FA355_VARIANTS_D64_D128(FA355_ROW, BF16, 64)
+    FA355_VARIANTS_D64_D128(FA355_ROW, BF16, 128)
+    FA355_VARIANTS_D256(FA355_ROW, BF16)
+    FA355_VARIANTS_D64_D128(FA355_ROW, F16, 64)
+    FA355_VARIANTS_D64_D128(FA355_ROW, F16, 128)
+    FA355_VARIANTS_D256(FA355_ROW, F16)
+    FA355_VARIANTS_F32(FA355_ROW_F32)
+};
+
+int elem_bytes(int dt) { return dt == FA355_F32 ? 4 : 2; }
+
+// The built-in tile (br, bc) for an input type and head dim.
+void default_tile(int dt, int d, int &br, int &bc)
+{
+    if (dt == FA355_F32) {
+        br = 32;
+        bc = 32;
+    } else if (d == 256) {
+        br = 128;
+        bc = 32;
+    } else {
+        br = 128;
+        bc = 64;
+    }
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+struct Checked {
+    const Variant *var;
+    fa355::FwdArgs args;
+    fa355_plan plan;
+};
+
+int validate(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+             int in_dt, int o_dt, const fa355_tuning *tuning, Checked &out)
+{
+    if (!q || !k || !v || !o)
+        return FA355_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+
+    if (in_dt != FA355_F32 && in_dt != FA355_F16 && in_dt != FA355_BF16)
+        return FA355_ERR_UNSUPPORTED;
+    if (!(o_dt == in_dt || (o_dt == FA355_F32 && in_dt != FA355_F32)))
+        return FA355_ERR_UNSUPPORTED;
+    if (in_dt == FA355_F32 ? d != 64 : (d != 64 && d != 128 && d != 256))
+        return FA355_ERR_UNSUPPORTED;
+
+    // One head must fit the kernels' 32-bit byte offsets.
+    const int64_t head_bytes = (int64_t)N * d * elem_bytes(in_dt);
+    if (head_bytes > INT_MAX - 65536)
+        return FA355_ERR_SHAPE;
+    if (!std::isfinite(scale))
+        return FA355_ERR_ARG;
+
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
+        reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(o) % 16 ||
+        reinterpret_cast<uintptr_t>(lse) % 4)
+        return FA355_ERR_ALIGN;
+
+    const size_t nq = (size_t)B * Hq * N * d, nkv = (size_t)B * Hkv * N * d;
+    const size_t bq = nq * elem_bytes(in_dt), bkv = nkv * elem_bytes(in_dt);
+    const size_t bo = nq * elem_bytes(o_dt), bl = (size_t)B * Hq * N * sizeof(float);
+    if (overlaps(o, bo, q, bq) || overlaps(o, bo, k, bkv) || overlaps(o, bo, v, bkv))
+        return FA355_ERR_ARG;
+    if (lse && (overlaps(lse, bl, q, bq) || overlaps(lse, bl, k, bkv) ||
+                overlaps(lse, bl, v, bkv) || overlaps(lse, bl, o, bo)))
+        return FA355_ERR_ARG;
+
+    int br, bc;
+    default_tile(in_dt, d, br, bc);
+    if (tuning && (tuning->br != 0 || tuning->bc != 0)) {
+        br = tuning->br;
+        bc = tuning->bc;
+    }
+    const bool want_f32 = o_dt == FA355_F32 && in_dt != FA355_F32;
+    const Variant *var = nullptr;
+    for (const Variant &x : kVariants)
+        if (x.dtype == in_dt && x.d == d && x.bc == bc && 32 * x.waves == br &&
+            x.causal == (causal != 0) && x.out_f32 == want_f32) {
+            var = &x;
+            break;
+        }
+    if (!var)
+        return FA355_ERR_UNSUPPORTED;
+
+    const int64_t n_qtiles = (N + br - 1) / br;
+    const int64_t tiles = (int64_t)B * Hq * n_qtiles;
+    if (tiles > INT_MAX)
+        return FA355_ERR_SHAPE;
+
+    fa355::FwdArgs &a = out.args;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = const_cast<void *>(o);
+    a.lse = const_cast<float *>(lse);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.group = Hq / Hkv;
+    a.n_qtiles = (int)n_qtiles;
+    a.total_tiles = (int)tiles;
+    // exp(x * scale) = exp2(x * scale * log2 e).  A negative scale is carried by
+    // negating Q (exact), so the multiplier is never negative; a zero or
+    // vanishing one is raised to the smallest normal float, which leaves every
+    // score at 0 after rounding and keeps -inf masks at -inf.
+    float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+    if (!(c >= 1.17549435e-38f))
+        c = 1.17549435e-38f;
+    a.c = c;
+    a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+
+    out.var = var;
+    out.plan.br = br;
+    out.plan.bc = bc;
+    out.plan.waves = var->waves;
+    out.plan.grid = (int)tiles;
+    out.plan.lds_bytes = var->lds;
+    return FA355_OK;
+}
+
+int run(const void *q, const void *k, const void *v, void *o, float *lse,
+        int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+        int in_dt, int o_dt, const fa355_tuning *tuning, hipStream_t stream)
+{
+    Checked c;
+    const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, in_dt, o_dt,
+                            tuning, c);
+    if (rc != FA355_OK)
+        return rc;
+    static const bool log = std::getenv("FA355_LOG") != nullptr;
+    if (log)
+        std::fprintf(stderr, "fa355: dtype=%d out_f32=%d d=%d causal=%d br=%d bc=%d grid=%d lds=%d\n",
+                     in_dt, (int)c.var->out_f32, d, causal != 0, c.plan.br, c.plan.bc,
+                     c.plan.grid, c.plan.lds_bytes);
+    return c.var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           fa355_dtype dtype, hipStream_t stream)
+{
+    return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, dtype, nullptr, stream);
+}
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+              fa355_dtype in_dtype, fa355_dtype o_dtype,
+              const fa355_tuning *tuning, hipStream_t stream)
+{
+    return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, in_dtype, o_dtype, tuning,
+               stream);
+}
+
+int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
+                 const float *lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                 float scale, fa355_dtype in_dtype, fa355_dtype o_dtype,
+                 const fa355_tuning *tuning, fa355_plan *plan)
+{
+    Checked c;
+    const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, in_dtype,
+                            o_dtype, tuning, c);
+    if (rc == FA355_OK && plan)
+        *plan = c.plan;
+    return rc;
+}
+
+const char *fa_status_str(int status)
+{
+    switch (status) {
+    case FA355_OK: return "ok";
+    case FA355_ERR_NULL: return "a required pointer is NULL";
+    case FA355_ERR_SHAPE: return "bad shape (sizes < 1, Hq % Hkv != 0, or too large)";
+    case FA355_ERR_UNSUPPORTED: return "unsupported head dim, dtype pair or tiling";
+    case FA355_ERR_ALIGN: return "misaligned pointer (16 bytes for tensors, 4 for lse)";
+    case FA355_ERR_ARG: return "bad argument (non-finite scale or overlapping buffers)";
+    case FA355_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// fa_args.hpp -- what the host passes to a kernel launch, the list of built
+// kernel variants, and the launcher declarations.  Host code includes only this;
+// the kernels themselves live in fa_fwd_kernel.hpp and are instantiated in the
+// shard files (fa_inst_*.hip).
+//
+// X(T, D, BC, WAVES, CAUSAL, OUT_F32) lists 16-bit-input variants; Y(WAVES, CAUSAL)
+// lists fp32-input variants (head dim 64, BC = 32).  The host table and the shard
+// files expand the same lists, so a variant missing from a shard is a link error.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fa355 {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, Hq, Hkv, N;
+    int group;         // Hq / Hkv: consecutive query heads per K/V head
+    int n_qtiles;      // ceil(N / BR)
+    int total_tiles;   // B * Hq * n_qtiles = grid size
+    float c;           // |scale| * log2(e); FLT_MIN stands in for a zero scale
+    uint32_t q_sign;   // 0x80008000 flips the sign of every 16-bit Q element
+};
+
+struct BF16 {};
+struct F16 {};
+
+// Launchers: one per kernel variant, explicitly instantiated in the shard files.
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+
+template <int WAVES, bool CAUSAL>
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+
+}  // namespace fa355
+
+// Head dims 64 and 128: default tile 128 x 64 (4 waves), plus tilings for tuning
+// and tests: 64 x 64, 128 x 32, 256 x 64.
+#define FA355_VARIANTS_D64_D128(X, T, D)                                              \
+    X(T, D, 64, 4, false, false) X(T, D, 64, 4, false, true)                          \
+    X(T, D, 64, 4, true, false)  X(T, D, 64, 4, true, true)                           \
+    X(T, D, 64, 2, false, false) X(T, D, 64, 2, true, false)                          \
+    X(T, D, 32, 4, false, false) X(T, D, 32, 4, true, false)                          \
+    X(T, D, 64, 8, false, false) X(T, D, 64, 8, true, false)
+
+// Head dim 256: default tile 128 x 32, plus 128 x 64.
+#define FA355_VARIANTS_D256(X, T)                                                     \
+    X(T, 256, 32, 4, false, false) X(T, 256, 32, 4, false, true)                      \
+    X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)                       \
+    X(T, 256, 64, 4, false, false) X(T, 256, 64, 4, true, false)
+
+#define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
+

@@ -1,0 +1,544 @@
+// fa_fwd_kernel.hpp -- fused FlashAttention forward kernels for gfx950 (CDNA4).
+//
+// One workgroup owns one tile of BR = 32*WAVES query rows of one (batch, query
+// head) and streams the key/value rows of the matching K/V head through LDS in
+// blocks of BC rows.  Each 64-lane wavefront owns 32 query rows.  For every
+// key/value block the wavefront
+//
+//   1. computes the transposed score tile S^T = K_blk Q_w^T (BC x 32) on the
+//      matrix cores (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation);
+//   2. masks keys past the causal diagonal or past N (only in blocks that need it);
+//   3. updates the running row maximum m, row sum l and output accumulator O by
+//      the online-softmax recurrence ("MCU 上 Transformer 模型的 Flash Attention
+//      实现…", §二, flowchart: m_new = max(m_old, rowmax S), P = exp(S - m_new),
+//      l_new = e^(m_old - m_new) l_old + rowsum P, O_new = e^(m_old - m_new) O_old + P V),
+//      in base 2 with the scale and log2(e) folded into one multiplier, and with the
+//      rescale of O and l skipped while the new block maximum stays within TAU of m
+//      (any stale m >= the true row maximum - TAU gives the same exact quotient O/l);
+//   4. accumulates O^T += V_blk^T P^T on the matrix cores, P rounded to the input
+//      type; the row sum l adds those same rounded values.
+//
+// O is normalised once after the last block (§三 of the same page, final
+// normalisation) and written with lse = ln 2 * (m + log2 l).  Nothing of size N x N
+// is ever stored ("FlashAttention (VI)", sections on tiling and kernel fusion).
+//
+// Register layouts (32x32 MFMA): lane L holds operand row/column L % 32 and the
+// eight consecutive k-slots 8*(L/32) .. 8*(L/32)+7; accumulator register r of lane L
+// holds row 8*(r/4) + 4*(L/32) + r%4 of column L % 32.  With the score tile
+// transposed, each lane owns one query row (its column), and a row's 2*16 scores sit
+// in lanes L and L^32: row reductions are in-lane plus one v_permlane32_swap.  The
+// same accumulator registers, converted to 16-bit, are directly the B operand of the
+// P.V product; V is stored transposed in LDS so that its A operand is one 16-byte
+// read per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_args.hpp"
+
+namespace fa355 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kTau = 8.0f;                 // lazy-rescale threshold, log2 units
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit dwords (gfx9 family)
+
+template <typename T> struct Mfma;
+template <> struct Mfma<BF16> {
+    // bf16 rounds P by up to 2^-8 relative, too coarse for a 1e-3 logsumexp: the
+    // lse keeps its own fp32 sum of the unrounded P.
+    static constexpr bool kSeparateLseSum = true;
+    static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    // Two fp32 values -> two bf16, round to nearest even (v_cvt_pk_bf16_f32).
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        f32x2_t v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+    // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against (1, 1)).
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), one, acc, false);
+    }
+};
+template <> struct Mfma<F16> {
+    static constexpr bool kSeparateLseSum = false;   // fp16 rounds P by <= 2^-11
+    static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    // Two fp32 values -> two fp16, round to nearest even (v_cvt_f16_f32).
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        f32x2_t v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+    // acc + lo + hi of a packed pair (v_dot2c_f32_f16 against (1, 1)).
+    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+        const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), one, acc, false);
+    }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// 16-byte load; offsets at or past the resource size read as zero.
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Values of lanes L and L^32 (same query row), in a fixed order on both lanes.
+__device__ __forceinline__ f32x2_t row_pair(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    f32x2_t r = {__uint_as_float(p[0]), __uint_as_float(p[1])};
+    return r;
+}
+
+// Work-item order.  Workgroup w runs on XCD w % 8 (round-robin dispatch), so the
+// w-th workgroup of each XCD is given the next tile of one contiguous range of
+// tiles: the query tiles of one (batch, head) -- and the query heads that share
+// its K/V head -- stay on one XCD and reuse K/V in its L2.  Within a head, causal
+// tiles go longest-first so the short ones fill the tail of the launch.
+__device__ __forceinline__ void tile_of(int w, int total, int n_qtiles, bool causal,
+                                        int &bh, int &qt) {
+    const int xcd = w & 7, s = w >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + s;
+    bh = L / n_qtiles;
+    qt = L - bh * n_qtiles;
+    if (causal)
+        qt = n_qtiles - 1 - qt;
+}
+
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
+struct FwdTraits {
+    static constexpr int BR = 32 * WAVES;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int DK = D / 16;            // 16-wide k chunks of Q K^T
+    static constexpr int NB = D / 32;            // 32-wide output column blocks
+    static constexpr int JB = BC / 32;           // 32-row blocks of the score tile
+    static constexpr int KS = BC / 16;           // 16-key steps of P V
+    static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+    static constexpr int K_TOTAL = BC * CPR;              // 16-byte K chunks per block
+    static constexpr int V_TOTAL = (BC / 4) * CPR;        // (4 rows x 1 chunk) V units
+    static constexpr int K_LOADS = (K_TOTAL + NT - 1) / NT;
+    static constexpr int V_UNITS = (V_TOTAL + NT - 1) / NT;
+    static constexpr int VT_CPR = BC / 8;        // 16-byte chunks per V^T row
+    static constexpr int K_SWZ = (CPR < 16 ? CPR : 16) - 1;
+    static constexpr int V_SWZ = VT_CPR - 1;
+    static constexpr int K_STAGE = BC * D * 2;
+    static constexpr int V_STAGE = D * BC * 2;
+    static constexpr int STAGE = K_STAGE + V_STAGE;
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+    static_assert(VT_CPR >= 4, "V^T row holds at least one 32-key block");
+};
+
+// Swizzle of the 16-byte chunk index within a V^T row (row = output column n):
+// distinct for 16 consecutive rows read together, and spread for the transposed
+// writes, whose lanes step n by 8.
+__device__ __forceinline__ int vt_swz(int n, int mask) { return (n ^ (n >> 3)) & mask; }
+
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
+__global__ void __launch_bounds__(64 * WAVES)
+fa_fwd_kernel(FwdArgs a)
+{
+    using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
+    using M = Mfma<T>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int h2 = lane >> 5;
+
+    int bh, qt;
+    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, CAUSAL, bh, qt);
+    const int b = bh / a.Hq;
+    const int hk = (bh - b * a.Hq) / a.group;
+    const int N = a.N;
+    const int i0 = qt * Tr::BR;
+    const int iw0 = i0 + wave * 32;             // this wavefront's first query row
+    const int iq = iw0 + l32;                   // this lane's query row
+    const int head_bytes = N * D * 2;
+
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const char *>(a.q) + (size_t)bh * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(static_cast<const char *>(a.k) + ((size_t)b * a.Hkv + hk) * head_bytes, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(static_cast<const char *>(a.v) + ((size_t)b * a.Hkv + hk) * head_bytes, head_bytes);
+
+    // Q fragments: B operand of S^T = K Q^T.  Rows past N read as zero.
+    u32x4_t qf[Tr::DK];
+#pragma unroll
+    for (int kk = 0; kk < Tr::DK; ++kk) {
+        qf[kk] = load16(rq, (iq * D + kk * 16 + h2 * 8) * 2);
+        qf[kk] ^= a.q_sign;
+    }
+
+    const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
+    const int n_kv = (kv_len + BC - 1) / BC;
+
+    // Register staging of the next K/V block (coalesced 16-byte loads).
+    u32x4_t kst[Tr::K_LOADS];
+    u32x4_t vst[Tr::V_UNITS][4];
+
+    auto load_block = [&](int t) {
+        const int j0 = t * BC;
+#pragma unroll
+        for (int c = 0; c < Tr::K_LOADS; ++c) {
+            const int id = c * Tr::NT + tid;
+            if (Tr::K_TOTAL % Tr::NT != 0 && id >= Tr::K_TOTAL)
+                break;
+            const int row = id / Tr::CPR, cc = id % Tr::CPR;
+            kst[c] = load16(rk, ((j0 + row) * D + cc * 8) * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < Tr::V_UNITS; ++u) {
+            const int id = u * Tr::NT + tid;
+            if (Tr::V_TOTAL % Tr::NT != 0 && id >= Tr::V_TOTAL)
+                break;
+            const int rg = id / Tr::CPR, cc = id % Tr::CPR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vst[u][e] = load16(rv, ((j0 + 4 * rg + e) * D + cc * 8) * 2);
+        }
+    };
+
+    auto store_block = [&](int stage) {
+        char *ks = smem + stage * Tr::STAGE;
+        char *vs = ks + Tr::K_STAGE;
+#pragma unroll
+        for (int c = 0; c < Tr::K_LOADS; ++c) {
+            const int id = c * Tr::NT + tid;
+            if (Tr::K_TOTAL % Tr::NT != 0 && id >= Tr::K_TOTAL)
+                break;
+            const int row = id / Tr::CPR, cc = id % Tr::CPR;
+            *reinterpret_cast<u32x4_t *>(ks + row * (D * 2) + ((cc ^ (row & Tr::K_SWZ)) << 4)) = kst[c];
+        }
+        // V^T: keys 4rg..4rg+3 of output column n become 8 bytes of row n.  Within
+        // each 16-key group the 4-key groups are stored in the order 0, 2, 1, 3, so
+        // that the eight keys one lane feeds to one P.V step are one 16-byte chunk.
+#pragma unroll
+        for (int u = 0; u < Tr::V_UNITS; ++u) {
+            const int id = u * Tr::NT + tid;
+            if (Tr::V_TOTAL % Tr::NT != 0 && id >= Tr::V_TOTAL)
+                break;
+            const int rg = id / Tr::CPR, cc = id % Tr::CPR;
+            const int g4 = rg & 3;
+            const int cl = 2 * (rg >> 2) + (g4 & 1);
+            const int half = g4 >> 1;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {        // dword qd holds columns 2qd, 2qd+1
+                const uint32_t x0 = vst[u][0][qd], x1 = vst[u][1][qd];
+                const uint32_t x2 = vst[u][2][qd], x3 = vst[u][3][qd];
+#pragma unroll
+                for (int hi = 0; hi < 2; ++hi) {
+                    const int n = cc * 8 + 2 * qd + hi;
+                    u32x2_t w;
+                    if (hi == 0) {
+                        w[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+                        w[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
+                    } else {
+                        w[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+                        w[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
+                    }
+                    const int phys = cl ^ vt_swz(n, Tr::V_SWZ);
+                    *reinterpret_cast<u32x2_t *>(vs + n * (BC * 2) + (phys << 4) + (half << 3)) = w;
+                }
+            }
+        }
+    };
+
+    f32x16_t oacc[Tr::NB];
+#pragma unroll
+    for (int nb = 0; nb < Tr::NB; ++nb)
+        oacc[nb] = f32x16_t{};
+    float m_run = -__builtin_inff();
+    float l_part = 0.0f;       // this lane's half of the row sum of rounded P
+    float le_part = 0.0f;      // fp32 sum of unrounded P, for lse (bf16 only)
+    const float c = a.c;
+
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+
+    for (int t = 0; t < n_kv; ++t) {
+        const int j0 = t * BC;
+        if (t + 1 < n_kv)
+            load_block(t + 1);
+
+        // Blocks wholly above this wavefront's causal diagonal, and wavefronts
+        // wholly past N, have nothing to add.
+        const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
+        if (active) {
+            const char *ks = smem + (t & 1) * Tr::STAGE;
+            const char *vs = ks + Tr::K_STAGE;
+
+            f32x16_t sacc[Tr::JB];
+#pragma unroll
+            for (int jb = 0; jb < Tr::JB; ++jb)
+                sacc[jb] = f32x16_t{};
+#pragma unroll
+            for (int kk = 0; kk < Tr::DK; ++kk) {
+#pragma unroll
+                for (int jb = 0; jb < Tr::JB; ++jb) {
+                    const int row = jb * 32 + l32;
+                    const int ch = kk * 2 + h2;
+                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
+                        ks + row * (D * 2) + ((ch ^ (row & Tr::K_SWZ)) << 4));
+                    sacc[jb] = M::run(kf, qf[kk], sacc[jb]);
+                }
+            }
+
+            if ((CAUSAL && j0 + BC - 1 > iw0) || j0 + BC > N) {
+#pragma unroll
+                for (int jb = 0; jb < Tr::JB; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = j0 + jb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        const bool vis = j < N && (!CAUSAL || j <= iq);
+                        sacc[jb][r] = vis ? sacc[jb][r] : -__builtin_inff();
+                    }
+            }
+
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int jb = 0; jb < Tr::JB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, sacc[jb][r]);
+            const f32x2_t mp = row_pair(mx);
+            const float mt = fmaxf(mp[0], mp[1]) * c;
+
+            if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_part *= alpha;
+                if constexpr (M::kSeparateLseSum)
+                    le_part *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < Tr::NB; ++nb)
+                    oacc[nb] *= alpha;
+                m_run = m_new;
+            }
+
+            u32x4_t pf[Tr::KS];
+#pragma unroll
+            for (int jb = 0; jb < Tr::JB; ++jb) {
+                float p[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_run));
+                    if constexpr (M::kSeparateLseSum)
+                        le_part += p[r];
+                }
+                // The row sum adds the rounded weights the P.V product uses, so O is
+                // an exact weighted mean of V rows with those weights.
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t pk = M::pack(p[8 * s + 2 * e], p[8 * s + 2 * e + 1]);
+                        pf[2 * jb + s][e] = pk;
+                        l_part = M::sum2(pk, l_part);
+                    }
+            }
+
+#pragma unroll
+            for (int nb = 0; nb < Tr::NB; ++nb) {
+                const int n = nb * 32 + l32;
+                const char *vrow = vs + n * (BC * 2);
+                const int sw = vt_swz(n, Tr::V_SWZ);
+#pragma unroll
+                for (int kstep = 0; kstep < Tr::KS; ++kstep) {
+                    const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(
+                        vrow + (((2 * kstep + h2) ^ sw) << 4));
+                    oacc[nb] = M::run(vf, pf[kstep], oacc[nb]);
+                }
+            }
+        }
+
+        if (t + 1 < n_kv)
+            store_block((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue: O = O / l, lse = ln2 * (m + log2 l).
+    const f32x2_t lp = row_pair(l_part);
+    const float l_tot = lp[0] + lp[1];
+    float le_tot = l_tot;
+    if constexpr (M::kSeparateLseSum) {
+        const f32x2_t ep = row_pair(le_part);
+        le_tot = ep[0] + ep[1];
+    }
+    if (iq < N) {
+        const float inv = 1.0f / l_tot;
+        const size_t orow = ((size_t)bh * N + iq) * D;
+#pragma unroll
+        for (int nb = 0; nb < Tr::NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n0 = nb * 32 + 8 * g + 4 * h2;
+                const float y0 = oacc[nb][4 * g + 0] * inv, y1 = oacc[nb][4 * g + 1] * inv;
+                const float y2 = oacc[nb][4 * g + 2] * inv, y3 = oacc[nb][4 * g + 3] * inv;
+                if constexpr (OUT_F32) {
+                    f32x4_t y = {y0, y1, y2, y3};
+                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.o) + orow + n0) = y;
+                } else {
+                    u32x2_t y = {M::pack(y0, y1), M::pack(y2, y3)};
+                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.o) + orow + n0) = y;
+                }
+            }
+        if (h2 == 0 && a.lse)
+            a.lse[(size_t)bh * N + iq] = kLn2 * (m_run + __log2f(le_tot));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs, head dim 64 (the small single-precision case): same algorithm on
+// v_mfma_f32_32x32x2_f32, which takes one element per lane and so needs no
+// transposed V: lane (n, half) reads V[j][n] straight from a row-major tile.
+// P stays in fp32.  One LDS stage; this variant exists for exactness, not speed.
+// ---------------------------------------------------------------------------
+template <int WAVES, bool CAUSAL>
+struct F32Traits {
+    static constexpr int D = 64;
+    static constexpr int BC = 32;
+    static constexpr int BR = 32 * WAVES;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int KP = D + 1;             // padded K row (floats)
+    static constexpr int K_FLOATS = BC * KP;
+    static constexpr int V_FLOATS = BC * D;
+    static constexpr int LDS = (K_FLOATS + V_FLOATS) * 4;
+};
+
+template <int WAVES, bool CAUSAL>
+__global__ void __launch_bounds__(64 * WAVES)
+fa_fwd_f32_kernel(FwdArgs a)
+{
+    using Tr = F32Traits<WAVES, CAUSAL>;
+    constexpr int D = Tr::D, BC = Tr::BC;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *kl = reinterpret_cast<float *>(smem);
+    float *vl = kl + Tr::K_FLOATS;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int h2 = lane >> 5;
+
+    int bh, qt;
+    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, CAUSAL, bh, qt);
+    const int b = bh / a.Hq;
+    const int hk = (bh - b * a.Hq) / a.group;
+    const int N = a.N;
+    const int i0 = qt * Tr::BR;
+    const int iw0 = i0 + wave * 32;
+    const int iq = iw0 + l32;
+    const float *qh = static_cast<const float *>(a.q) + (size_t)bh * N * D;
+    const float *kh = static_cast<const float *>(a.k) + ((size_t)b * a.Hkv + hk) * N * D;
+    const float *vh = static_cast<const float *>(a.v) + ((size_t)b * a.Hkv + hk) * N * D;
+    const float qsign = a.q_sign ? -1.0f : 1.0f;
+
+    float qf[D / 2];
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk)
+        qf[kk] = iq < N ? qsign * qh[(size_t)iq * D + 2 * kk + h2] : 0.0f;
+
+    const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
+    const int n_kv = (kv_len + BC - 1) / BC;
+
+    f32x16_t oacc[2] = {f32x16_t{}, f32x16_t{}};
+    float m_run = -__builtin_inff();
+    float l_part = 0.0f;
+    const float c = a.c;
+
+    for (int t = 0; t < n_kv; ++t) {
+        const int j0 = t * BC;
+        __syncthreads();
+        for (int x = tid; x < BC * D; x += Tr::NT) {
+            const int row = x / D, col = x % D;
+            const bool in = j0 + row < N;
+            kl[row * Tr::KP + col] = in ? kh[(size_t)(j0 + row) * D + col] : 0.0f;
+            vl[row * D + col] = in ? vh[(size_t)(j0 + row) * D + col] : 0.0f;
+        }
+        __syncthreads();
+
+        const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
+        if (!active)
+            continue;
+
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < D / 2; ++kk)
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(kl[l32 * Tr::KP + 2 * kk + h2], qf[kk], s, 0, 0, 0);
+
+        if ((CAUSAL && j0 + BC - 1 > iw0) || j0 + BC > N) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                const bool vis = j < N && (!CAUSAL || j <= iq);
+                s[r] = vis ? s[r] : -__builtin_inff();
+            }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            mx = fmaxf(mx, s[r]);
+        const f32x2_t mp = row_pair(mx);
+        const float mt = fmaxf(mp[0], mp[1]) * c;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_part *= alpha;
+            oacc[0] *= alpha;
+            oacc[1] *= alpha;
+            m_run = m_new;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_run));
+            l_part += p;
+            const int j = 8 * (r >> 2) + 4 * h2 + (r & 3);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[j * D + nb * 32 + l32], p, oacc[nb], 0, 0, 0);
+        }
+    }
+
+    const f32x2_t lp = row_pair(l_part);
+    const float l_tot = lp[0] + lp[1];
+    if (iq < N) {
+        const float inv = 1.0f / l_tot;
+        float *orow = static_cast<float *>(a.o) + ((size_t)bh * N + iq) * D;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4_t y = {oacc[nb][4 * g] * inv, oacc[nb][4 * g + 1] * inv,
+                             oacc[nb][4 * g + 2] * inv, oacc[nb][4 * g + 3] * inv};
+                *reinterpret_cast<f32x4_t *>(orow + nb * 32 + 8 * g + 4 * h2) = y;
+            }
+        if (h2 == 0 && a.lse)
+            a.lse[(size_t)bh * N + iq] = kLn2 * (m_run + __log2f(l_tot));
+    }
+}
+
+}  // namespace fa355

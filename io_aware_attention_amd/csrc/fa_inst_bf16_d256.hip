@@ -1,0 +1,4 @@
+// Kernel variants for bf16 inputs, head dim 256.
+#include "fa_launch.hpp"
+
+FA355_VARIANTS_D256(FA355_INSTANTIATE, BF16)

@@ -1,0 +1,4 @@
+// Kernel variants for f16 inputs, head dim 128.
+#include "fa_launch.hpp"
+
+FA355_VARIANTS_D64_D128(FA355_INSTANTIATE, F16, 128)

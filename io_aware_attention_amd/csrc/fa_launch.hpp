@@ -1,0 +1,37 @@
+// fa_launch.hpp -- launcher definitions; included by the shard files only.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa355 {
+
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
+{
+    using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, OUT_F32>);
+    static const hipError_t attr =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS);
+    if (attr != hipSuccess)
+        return attr;
+    FwdArgs arg = a;
+    void *params[] = {&arg};
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, Tr::LDS, stream);
+}
+
+template <int WAVES, bool CAUSAL>
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
+{
+    using Tr = F32Traits<WAVES, CAUSAL>;
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_f32_kernel<WAVES, CAUSAL>);
+    FwdArgs arg = a;
+    void *params[] = {&arg};
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, Tr::LDS, stream);
+}
+
+}  // namespace fa355
+
+#define FA355_INSTANTIATE(T, D, BC, W, C, O)                                          \
+    template hipError_t fa355::launch_fwd<fa355::T, D, BC, W, C, O>(const fa355::FwdArgs &, hipStream_t);
+#define FA355_INSTANTIATE_F32(W, C)                                                   \
+    template hipError_t fa355::launch_fwd_f32<W, C>(const fa355::FwdArgs &, hipStream_t);

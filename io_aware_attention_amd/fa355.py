@@ -1,0 +1,151 @@
+"""ctypes binding of libfa355 -- argument marshalling only.
+
+Every step of the attention forward pass runs in the library's HIP kernels; this
+module only turns torch tensors into pointers, sizes and a stream, and turns
+status codes into exceptions.  torch provides device memory and streams.  If the
+built library is missing, importing the binding's functions raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa355.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+
+# Every exported symbol, as declared in include/fa355.h.
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_status_str", "fa_version")
+
+
+class FA355Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"fa355 error {status}: {msg}")
+        self.status = status
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int), ("waves", ctypes.c_int),
+                ("grid", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FA355Error(ERR_HIP, f"{LIB_PATH} is not built; run "
+                         "`python -m io_aware_attention_amd.build` first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ip, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    common = [vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, fp]
+    L.fa_fwd.argtypes = common + [ip, vp]
+    L.fa_fwd.restype = ip
+    L.fa_fwd_ex.argtypes = common + [ip, ip, ctypes.POINTER(Tuning), vp]
+    L.fa_fwd_ex.restype = ip
+    L.fa_fwd_check.argtypes = common + [ip, ip, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
+    L.fa_fwd_check.restype = ip
+    L.fa_status_str.argtypes = [ip]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = ip
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise FA355Error(rc, status_str(rc))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t not in codes:
+        raise FA355Error(ERR_UNSUPPORTED, f"dtype {t} not supported")
+    return codes[t]
+
+
+def _tuning(tuning):
+    if tuning is None:
+        return None
+    br, bc = tuning
+    return ctypes.byref(Tuning(int(br), int(bc)))
+
+
+def plan(B, Hq, Hkv, N, d, causal, dtype, out_dtype=None, tuning=None, scale=None) -> Plan:
+    """The launch fa_fwd_ex would make for these sizes (no GPU needed)."""
+    dt = _dtype_code(dtype)
+    odt = dt if out_dtype is None else _dtype_code(out_dtype)
+    p = Plan()
+    fake = 1 << 40  # distinct, 16-byte-aligned host addresses: only compared, never read
+    span = B * max(Hq, Hkv) * N * d * 8 + 4096
+    rc = lib().fa_fwd_check(fake, fake + span, fake + 2 * span, fake + 3 * span,
+                            fake + 4 * span, B, Hq, Hkv, N, d, int(bool(causal)),
+                            float(1.0 / math.sqrt(d) if scale is None else scale),
+                            dt, odt, _tuning(tuning), ctypes.byref(p))
+    _check(rc)
+    return p
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out_dtype=None,
+        o=None, lse=None, return_lse: bool = True, tuning=None, stream=None):
+    """Attention forward on torch device tensors.
+
+    q: [B,Hq,N,d]; k, v: [B,Hkv,N,d]; all contiguous, same dtype (fp32, fp16 or
+    bf16).  scale defaults to 1/sqrt(d).  out_dtype may be torch.float32 for 16-bit
+    inputs.  o / lse may be given (preallocated); otherwise they are allocated
+    with torch.  tuning is an optional (br, bc).  Returns (o, lse) (lse is None when
+    return_lse is False).  The kernel runs on `stream` (default: torch's current
+    stream); the call returns once it is enqueued.
+    """
+    import torch
+    L = lib()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FA355Error(ERR_SHAPE, "q, k, v must be 4-D [B,H,N,d]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    dt = _dtype_code(q.dtype)
+    odt_t = q.dtype if out_dtype is None else out_dtype
+    odt = _dtype_code(odt_t)
+    if o is None:
+        o = torch.empty((B, Hq, N, d), dtype=odt_t, device=q.device)
+    elif tuple(o.shape) != (B, Hq, N, d) or o.dtype != odt_t or not o.is_contiguous():
+        raise FA355Error(ERR_ARG, "o has the wrong shape, dtype or layout")
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise FA355Error(ERR_ARG, "lse has the wrong shape, dtype or layout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                     None if lse is None else lse.data_ptr(),
+                     B, Hq, Hkv, N, d, int(bool(causal)), float(scale), dt, odt,
+                     _tuning(tuning), ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse

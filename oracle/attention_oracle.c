@@ -148,23 +148,28 @@ static void *worker(void *arg)
 
 static int run_job(oracle_job *J, int threads)
 {
-    /* Keep each thread's score block at or below 64 MB. */
-    int64_t chunk = (64LL << 20) / (8 * J->N);
-    if (chunk < 1)
-        chunk = 1;
-    if (chunk > J->nrows)
-        chunk = J->nrows;
-    J->chunk = chunk;
-    J->units_per_bh = (J->nrows + chunk - 1) / chunk;
-    J->nunits = J->B * J->Hq * J->units_per_bh;
-    J->next = 0;
-    J->failed = 0;
-    pthread_mutex_init(&J->mu, NULL);
-
     if (threads <= 0)
         threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
     if (threads < 1)
         threads = 1;
+
+    /* Rows per work unit: enough units to keep every thread busy (about four per
+     * thread), and each thread's score block at or below 64 MB. */
+    const int64_t heads = J->B * J->Hq;
+    const int64_t want = (4LL * threads + heads - 1) / heads;
+    int64_t chunk = (J->nrows + want - 1) / want;
+    const int64_t cap = (64LL << 20) / (8 * J->N);
+    if (chunk > cap)
+        chunk = cap;
+    if (chunk < 1)
+        chunk = 1;
+    J->chunk = chunk;
+    J->units_per_bh = (J->nrows + chunk - 1) / chunk;
+    J->nunits = heads * J->units_per_bh;
+    J->next = 0;
+    J->failed = 0;
+    pthread_mutex_init(&J->mu, NULL);
+
     if (threads > J->nunits)
         threads = (int)J->nunits;
 

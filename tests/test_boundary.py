@@ -1,0 +1,103 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and its
+validation rejects every bad argument before touching HIP (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_attention_amd as F
+from io_aware_attention_amd import fa355 as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+BASE = 1 << 40      # fake, aligned, never dereferenced addresses
+SPAN = 1 << 32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = F.lib()
+    assert L.fa_version() == 100
+    for s in range(-6, 1):
+        assert F.status_str(s) and F.status_str(s) != "unknown status"
+    assert F.status_str(-99) == "unknown status"
+
+
+def check(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+          B_=1, Hq=4, Hkv=2, N=100, d=128, causal=1, scale=0.1, dt=F.BF16, odt=None,
+          tuning=None):
+    p = B.Plan()
+    t = None if tuning is None else ctypes.byref(B.Tuning(*tuning))
+    rc = F.lib().fa_fwd_check(q, k, v, o, lse, B_, Hq, Hkv, N, d, causal, scale, dt,
+                              dt if odt is None else odt, t, ctypes.byref(p))
+    return rc, p
+
+
+def test_valid_call_plans_a_launch():
+    rc, p = check(B_=1, Hq=32, Hkv=32, N=4096, d=128)
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 64, 4, 1024)
+    assert p.lds_bytes == 2 * 2 * 64 * 128 * 2
+    rc, p = check(B_=4, Hq=32, Hkv=8, N=8192)
+    assert rc == 0 and p.grid == 4 * 32 * 64
+    rc, p = check(B_=1, Hq=1, Hkv=1, N=128, d=64, dt=F.F32, tuning=(32, 32))
+    assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
+    rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
+    assert rc == 0 and (p.br, p.bc) == (128, 32)
+    rc, p = check(lse=None)
+    assert rc == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(B_=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(N=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(N=-5), -2), (dict(N=1 << 30), -2),
+    (dict(d=96), -3), (dict(d=32), -3), (dict(d=512), -3), (dict(dt=F.F32, d=128), -3),
+    (dict(dt=7), -3), (dict(odt=F.F16), -3), (dict(dt=F.F32, d=64, odt=F.BF16), -3),
+    (dict(tuning=(96, 64)), -3), (dict(tuning=(128, 48)), -3),
+    (dict(dt=F.F32, d=64, tuning=(128, 64)), -3),
+    (dict(scale=float("inf")), -5), (dict(scale=float("nan")), -5),
+    (dict(q=BASE + 2), -4), (dict(o=BASE + 3 * SPAN + 8), -4), (dict(lse=BASE + 4 * SPAN + 2), -4),
+    (dict(o=BASE), -5), (dict(o=BASE + SPAN + 4096), -5), (dict(lse=BASE + 2 * SPAN + 64), -5),
+    (dict(lse=BASE + 3 * SPAN), -5),
+])
+def test_rejections(kw, code):
+    rc, _ = check(**kw)
+    assert rc == code, (kw, rc)
+
+
+def test_fwd_validates_before_any_hip_call():
+    # Invalid arguments return their code from fa_fwd / fa_fwd_ex without a GPU.
+    L = F.lib()
+    assert L.fa_fwd(None, BASE, BASE, BASE, None, 1, 1, 1, 8, 128, 0, 1.0, F.BF16, None) == -1
+    assert L.fa_fwd(BASE, BASE, BASE, BASE + SPAN, None, 1, 1, 1, 8, 96, 0, 1.0, F.BF16, None) == -3
+    assert L.fa_fwd_ex(BASE, BASE, BASE, BASE, None, 1, 1, 1, 8, 128, 0, 1.0, F.BF16, F.BF16,
+                       None, None) == -5
+
+
+def test_fp32_output_allowed_for_16_bit_inputs():
+    assert check(odt=F.F32)[0] == 0
+    assert check(dt=F.F16, odt=F.F32)[0] == 0
+    assert check(dt=F.F32, d=64, odt=F.F32)[0] == 0
+
+
+def test_python_plan_helper():
+    import torch
+    p = F.plan(16, 16, 16, 512, 64, False, torch.float16)
+    assert p.grid == 16 * 16 * 4
+    with pytest.raises(F.FA355Error):
+        F.plan(1, 1, 1, 8, 80, False, torch.bfloat16)
