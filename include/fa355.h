@@ -95,8 +95,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *   o_dtype   the output element type: in_dtype, or FA355_F32 for F16/BF16 inputs
  *             (identical arithmetic; only the final store differs)
  *   tuning    NULL or {0,0} for the default tiles, else one of the built tilings
- *             (br, bc) in {(128,64), (64,64), (128,32), (256,64)} for F16/BF16 and
- *             {(32,32), (64,32), (128,32)} for F32
+ *             (br, bc): for F16/BF16 with d = 64 or 128, (128,64), (128,32), (256,64)
+ *             (also with F32 output) and (64,64); with d = 256, (128,64), (128,32);
+ *             for F32, (32,32), (64,32), (128,32)
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int Hq, int Hkv, int N, int d, int causal, float scale,

@@ -31,7 +31,7 @@ struct Variant {
 #define FA355_DT_BF16 FA355_BF16
 #define FA355_DT_F16 FA355_F16
 #define FA355_ROW(T, D, BC, W, C, O) \
-    {FA355_DT_##T, D, BC, W, C, O, 8 * (BC) * (D), &fa355::launch_fwd<fa355::T, D, BC, W, C, O>},
+    {FA355_DT_##T, D, BC, W, C, O, fa355::fwd_lds_bytes(D, BC), &fa355::launch_fwd<fa355::T, D, BC, W, C, O>},
 #define FA355_ROW_F32(W, C) \
     {FA355_F32, 64, 32, W, C, false, (32 * 65 + 32 * 64) * 4, &fa355::launch_fwd_f32<W, C>},
 
@@ -47,15 +47,21 @@ const Variant kVariants[] = {
 
 int elem_bytes(int dt) { return dt == FA355_F32 ? 4 : 2; }
 
-// The built-in tile (br, bc) for an input type and head dim.
-void default_tile(int dt, int d, int &br, int &bc)
+// The built-in tile (br, bc) for an input type, head dim and sequence length,
+// chosen by measurement on MI355X.  Long sequences amortise a block's loads over
+// 256 query rows; shorter ones keep 128-row tiles with 32-key blocks, whose lower
+// register use fits three wavefronts per SIMD.
+void default_tile(int dt, int d, int N, int &br, int &bc)
 {
     if (dt == FA355_F32) {
         br = 32;
         bc = 32;
     } else if (d == 256) {
         br = 128;
-        bc = 32;
+        bc = 64;
+    } else if (d == 128) {
+        br = N >= 8192 ? 256 : 128;
+        bc = N >= 8192 ? 64 : 32;
     } else {
         br = 128;
         bc = 64;
@@ -112,7 +118,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
         return FA355_ERR_ARG;
 
     int br, bc;
-    default_tile(in_dt, d, br, bc);
+    default_tile(in_dt, d, N, br, bc);
     if (tuning && (tuning->br != 0 || tuning->bc != 0)) {
         br = tuning->br;
         bc = tuning->bc;

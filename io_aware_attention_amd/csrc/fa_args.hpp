@@ -13,6 +13,10 @@
 
 namespace fa355 {
 
+// LDS bytes of a 16-bit-input kernel: two stages of a K block (BC rows of 2D bytes)
+// and a transposed V block (D rows of 2BC bytes), every row padded by 16 bytes.
+constexpr int fwd_lds_bytes(int D, int BC) { return 2 * (BC * (2 * D + 16) + D * (2 * BC + 16)); }
+
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
@@ -37,20 +41,22 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 
 }  // namespace fa355
 
-// Head dims 64 and 128: default tile 128 x 64 (4 waves), plus tilings for tuning
-// and tests: 64 x 64, 128 x 32, 256 x 64.
+// Head dims 64 and 128: tiles 128 x 64, 128 x 32 and 256 x 64 (each also with fp32
+// output), and 64 x 64.
 #define FA355_VARIANTS_D64_D128(X, T, D)                                              \
     X(T, D, 64, 4, false, false) X(T, D, 64, 4, false, true)                          \
     X(T, D, 64, 4, true, false)  X(T, D, 64, 4, true, true)                           \
-    X(T, D, 64, 2, false, false) X(T, D, 64, 2, true, false)                          \
-    X(T, D, 32, 4, false, false) X(T, D, 32, 4, true, false)                          \
-    X(T, D, 64, 8, false, false) X(T, D, 64, 8, true, false)
+    X(T, D, 32, 4, false, false) X(T, D, 32, 4, false, true)                          \
+    X(T, D, 32, 4, true, false)  X(T, D, 32, 4, true, true)                           \
+    X(T, D, 64, 8, false, false) X(T, D, 64, 8, false, true)                          \
+    X(T, D, 64, 8, true, false)  X(T, D, 64, 8, true, true)                           \
+    X(T, D, 64, 2, false, false) X(T, D, 64, 2, true, false)
 
-// Head dim 256: default tile 128 x 32, plus 128 x 64.
+// Head dim 256: tiles 128 x 64 and 128 x 32, each also with fp32 output.
 #define FA355_VARIANTS_D256(X, T)                                                     \
+    X(T, 256, 64, 4, false, false) X(T, 256, 64, 4, false, true)                      \
+    X(T, 256, 64, 4, true, false)  X(T, 256, 64, 4, true, true)                       \
     X(T, 256, 32, 4, false, false) X(T, 256, 32, 4, false, true)                      \
-    X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)                       \
-    X(T, 256, 64, 4, false, false) X(T, 256, 64, 4, true, false)
+    X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)
 
 #define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
-

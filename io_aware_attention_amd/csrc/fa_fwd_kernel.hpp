@@ -107,20 +107,35 @@ __device__ __forceinline__ f32x2_t row_pair(float x) {
     return r;
 }
 
-// Work-item order.  Workgroup w runs on XCD w % 8 (round-robin dispatch), so the
-// w-th workgroup of each XCD is given the next tile of one contiguous range of
-// tiles: the query tiles of one (batch, head) -- and the query heads that share
-// its K/V head -- stay on one XCD and reuse K/V in its L2.  Within a head, causal
-// tiles go longest-first so the short ones fill the tail of the launch.
-__device__ __forceinline__ void tile_of(int w, int total, int n_qtiles, bool causal,
+// Work-item order.  Workgroup w runs on XCD w % 8 (round-robin dispatch); the
+// w-th workgroup of each XCD takes the next index of one contiguous range, so each
+// XCD sees a contiguous slice of the logical order below.  The logical order cuts
+// the B*Hq heads into groups of about B*Hq/8 consecutive heads (one group per XCD,
+// so a group's K/V -- shared by consecutive GQA query heads -- stays in one L2),
+// and walks each group query-tile-major: for causal attention the longest tiles of
+// all the group's heads go first (longest-processing-time order), which lets the
+// short tiles fill in the end of the launch evenly.
+__device__ __forceinline__ void tile_of(int w, int total, int n_qtiles, int heads, bool causal,
                                         int &bh, int &qt) {
     const int xcd = w & 7, s = w >> 3;
     const int per = total >> 3, rem = total & 7;
     const int L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + s;
-    bh = L / n_qtiles;
-    qt = L - bh * n_qtiles;
-    if (causal)
-        qt = n_qtiles - 1 - qt;
+    const int gh = heads >= 8 ? heads >> 3 : 1;          // heads per group
+    const int full = (heads / gh) * gh * n_qtiles;       // tiles in whole groups
+    int r, g0, gn;
+    if (L < full) {
+        const int g = L / (gh * n_qtiles);
+        r = L - g * gh * n_qtiles;
+        g0 = g * gh;
+        gn = gh;
+    } else {
+        r = L - full;
+        g0 = (heads / gh) * gh;
+        gn = heads - g0;
+    }
+    const int rank = r / gn;
+    bh = g0 + (r - rank * gn);
+    qt = causal ? n_qtiles - 1 - rank : rank;
 }
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
@@ -132,28 +147,31 @@ struct FwdTraits {
     static constexpr int JB = BC / 32;           // 32-row blocks of the score tile
     static constexpr int KS = BC / 16;           // 16-key steps of P V
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-    static constexpr int K_TOTAL = BC * CPR;              // 16-byte K chunks per block
-    static constexpr int V_TOTAL = (BC / 4) * CPR;        // (4 rows x 1 chunk) V units
+    static constexpr int RG = BC / 4;            // 4-row groups per V block
+    static constexpr int K_TOTAL = BC * CPR;     // 16-byte K chunks per block
+    static constexpr int V_TOTAL = RG * CPR;     // (4 rows x 1 chunk) V units per block
     static constexpr int K_LOADS = (K_TOTAL + NT - 1) / NT;
     static constexpr int V_UNITS = (V_TOTAL + NT - 1) / NT;
-    static constexpr int VT_CPR = BC / 8;        // 16-byte chunks per V^T row
-    static constexpr int K_SWZ = (CPR < 16 ? CPR : 16) - 1;
-    static constexpr int V_SWZ = VT_CPR - 1;
-    static constexpr int K_STAGE = BC * D * 2;
-    static constexpr int V_STAGE = D * BC * 2;
+    // LDS rows are padded by 16 bytes: consecutive rows then start 4 banks apart,
+    // so the 16-byte reads of 8 (or 16) consecutive rows hit distinct banks, and
+    // every read address is one per-lane base plus a compile-time offset.
+    static constexpr int K_PITCH = D * 2 + 16;   // K row j: D keys' worth of bytes
+    static constexpr int V_PITCH = BC * 2 + 16;  // V^T row n: BC keys
+    static constexpr int K_STAGE = BC * K_PITCH;
+    static constexpr int V_STAGE = D * V_PITCH;
     static constexpr int STAGE = K_STAGE + V_STAGE;
     static constexpr int LDS = 2 * STAGE;
+    static_assert(LDS == fwd_lds_bytes(D, BC), "LDS size");
+    // Waves per SIMD to fit: two lets one wavefront's softmax run under the other's
+    // matrix work; head dim 256 needs the whole register file for one.
+    static constexpr int OCC = (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-    static_assert(VT_CPR >= 4, "V^T row holds at least one 32-key block");
+    static_assert(NT % RG == 0, "V load split");
 };
-
-// Swizzle of the 16-byte chunk index within a V^T row (row = output column n):
-// distinct for 16 consecutive rows read together, and spread for the transposed
-// writes, whose lanes step n by 8.
-__device__ __forceinline__ int vt_swz(int n, int mask) { return (n ^ (n >> 3)) & mask; }
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
 __global__ void __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC)))
 fa_fwd_kernel(FwdArgs a)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
@@ -161,109 +179,111 @@ fa_fwd_kernel(FwdArgs a)
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
 
     int bh, qt;
-    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, CAUSAL, bh, qt);
+    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, a.B * a.Hq, CAUSAL, bh, qt);
     const int b = bh / a.Hq;
     const int hk = (bh - b * a.Hq) / a.group;
     const int N = a.N;
     const int i0 = qt * Tr::BR;
     const int iw0 = i0 + wave * 32;             // this wavefront's first query row
     const int iq = iw0 + l32;                   // this lane's query row
-    const int head_bytes = N * D * 2;
+    constexpr int ROW = D * 2;                  // bytes per K/V/Q row
+    const int head_bytes = N * ROW;
 
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(static_cast<const char *>(a.q) + (size_t)bh * head_bytes, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(static_cast<const char *>(a.k) + ((size_t)b * a.Hkv + hk) * head_bytes, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(static_cast<const char *>(a.v) + ((size_t)b * a.Hkv + hk) * head_bytes, head_bytes);
+    const char *qh = static_cast<const char *>(a.q) + (size_t)bh * head_bytes;
+    const char *kh = static_cast<const char *>(a.k) + ((size_t)b * a.Hkv + hk) * head_bytes;
+    const char *vh = static_cast<const char *>(a.v) + ((size_t)b * a.Hkv + hk) * head_bytes;
 
     // Q fragments: B operand of S^T = K Q^T.  Rows past N read as zero.
     u32x4_t qf[Tr::DK];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, head_bytes);
 #pragma unroll
-    for (int kk = 0; kk < Tr::DK; ++kk) {
-        qf[kk] = load16(rq, (iq * D + kk * 16 + h2 * 8) * 2);
-        qf[kk] ^= a.q_sign;
+        for (int kk = 0; kk < Tr::DK; ++kk) {
+            qf[kk] = load16(rq, iq * ROW + (kk * 16 + h2 * 8) * 2);
+            qf[kk] ^= a.q_sign;
+        }
     }
 
     const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
     const int n_kv = (kv_len + BC - 1) / BC;
 
-    // Register staging of the next K/V block (coalesced 16-byte loads).
+    // Global -> register staging of the next block.  K: 16 consecutive lanes read
+    // one 256-byte row.  V: thread (4-row group rg, 16-byte column chunk cc), rg
+    // fastest, so that its transposed LDS writes from 16 lanes fill one V^T row.
+    const int k_row0 = tid / Tr::CPR, k_cc = tid % Tr::CPR;
+    const int v_rg = tid % Tr::RG, v_cc0 = tid / Tr::RG;
+    const int k_voff = k_row0 * ROW + k_cc * 16;
+    const int v_voff = 4 * v_rg * ROW + v_cc0 * 16;
     u32x4_t kst[Tr::K_LOADS];
     u32x4_t vst[Tr::V_UNITS][4];
 
     auto load_block = [&](int t) {
+        // The block's rows start the buffer, so rows past N read as zero.
         const int j0 = t * BC;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)j0 * ROW, (N - j0) * ROW);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)j0 * ROW, (N - j0) * ROW);
 #pragma unroll
         for (int c = 0; c < Tr::K_LOADS; ++c) {
-            const int id = c * Tr::NT + tid;
-            if (Tr::K_TOTAL % Tr::NT != 0 && id >= Tr::K_TOTAL)
+            if (Tr::K_TOTAL % Tr::NT != 0 && c * Tr::NT + tid >= Tr::K_TOTAL)
                 break;
-            const int row = id / Tr::CPR, cc = id % Tr::CPR;
-            kst[c] = load16(rk, ((j0 + row) * D + cc * 8) * 2);
+            kst[c] = load16(rk, k_voff + c * (Tr::NT / Tr::CPR) * ROW);
         }
 #pragma unroll
         for (int u = 0; u < Tr::V_UNITS; ++u) {
-            const int id = u * Tr::NT + tid;
-            if (Tr::V_TOTAL % Tr::NT != 0 && id >= Tr::V_TOTAL)
+            if (Tr::V_TOTAL % Tr::NT != 0 && u * Tr::NT + tid >= Tr::V_TOTAL)
                 break;
-            const int rg = id / Tr::CPR, cc = id % Tr::CPR;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                vst[u][e] = load16(rv, ((j0 + 4 * rg + e) * D + cc * 8) * 2);
+                vst[u][e] = load16(rv, v_voff + e * ROW + u * (Tr::NT / Tr::RG) * 16);
         }
     };
+
+    // LDS write addresses (per lane, loop-invariant).
+    const int k_wr = k_row0 * Tr::K_PITCH + k_cc * 16;
+    // V^T: keys 4rg..4rg+3 of output column n become 8 bytes of row n.  Within each
+    // 16-key group the 4-key groups are stored in the order 0, 2, 1, 3, so that the
+    // eight keys one lane feeds to one P.V step are one 16-byte chunk.
+    const int v_g4 = v_rg & 3;
+    const int v_wr = (v_cc0 * 8) * Tr::V_PITCH + (v_rg >> 2) * 32 + (v_g4 & 1) * 16 + (v_g4 >> 1) * 8;
 
     auto store_block = [&](int stage) {
         char *ks = smem + stage * Tr::STAGE;
         char *vs = ks + Tr::K_STAGE;
 #pragma unroll
         for (int c = 0; c < Tr::K_LOADS; ++c) {
-            const int id = c * Tr::NT + tid;
-            if (Tr::K_TOTAL % Tr::NT != 0 && id >= Tr::K_TOTAL)
+            if (Tr::K_TOTAL % Tr::NT != 0 && c * Tr::NT + tid >= Tr::K_TOTAL)
                 break;
-            const int row = id / Tr::CPR, cc = id % Tr::CPR;
-            *reinterpret_cast<u32x4_t *>(ks + row * (D * 2) + ((cc ^ (row & Tr::K_SWZ)) << 4)) = kst[c];
+            *reinterpret_cast<u32x4_t *>(ks + k_wr + c * (Tr::NT / Tr::CPR) * Tr::K_PITCH) = kst[c];
         }
-        // V^T: keys 4rg..4rg+3 of output column n become 8 bytes of row n.  Within
-        // each 16-key group the 4-key groups are stored in the order 0, 2, 1, 3, so
-        // that the eight keys one lane feeds to one P.V step are one 16-byte chunk.
 #pragma unroll
         for (int u = 0; u < Tr::V_UNITS; ++u) {
-            const int id = u * Tr::NT + tid;
-            if (Tr::V_TOTAL % Tr::NT != 0 && id >= Tr::V_TOTAL)
+            if (Tr::V_TOTAL % Tr::NT != 0 && u * Tr::NT + tid >= Tr::V_TOTAL)
                 break;
-            const int rg = id / Tr::CPR, cc = id % Tr::CPR;
-            const int g4 = rg & 3;
-            const int cl = 2 * (rg >> 2) + (g4 & 1);
-            const int half = g4 >> 1;
+            char *vw = vs + v_wr + u * (Tr::NT / Tr::RG) * 8 * Tr::V_PITCH;
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {        // dword qd holds columns 2qd, 2qd+1
                 const uint32_t x0 = vst[u][0][qd], x1 = vst[u][1][qd];
                 const uint32_t x2 = vst[u][2][qd], x3 = vst[u][3][qd];
-#pragma unroll
-                for (int hi = 0; hi < 2; ++hi) {
-                    const int n = cc * 8 + 2 * qd + hi;
-                    u32x2_t w;
-                    if (hi == 0) {
-                        w[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-                        w[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-                    } else {
-                        w[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-                        w[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-                    }
-                    const int phys = cl ^ vt_swz(n, Tr::V_SWZ);
-                    *reinterpret_cast<u32x2_t *>(vs + n * (BC * 2) + (phys << 4) + (half << 3)) = w;
-                }
+                u32x2_t lo, hi;
+                lo[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+                lo[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
+                hi[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+                hi[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
+                *reinterpret_cast<u32x2_t *>(vw + (2 * qd) * Tr::V_PITCH) = lo;
+                *reinterpret_cast<u32x2_t *>(vw + (2 * qd + 1) * Tr::V_PITCH) = hi;
             }
         }
     };
+
+    // LDS read bases (per lane): K row l32 chunk h2, V^T row l32 chunk h2.
+    const int k_rd = l32 * Tr::K_PITCH + h2 * 16;
+    const int v_rd = Tr::K_STAGE + l32 * Tr::V_PITCH + h2 * 16;
 
     f32x16_t oacc[Tr::NB];
 #pragma unroll
@@ -287,8 +307,8 @@ fa_fwd_kernel(FwdArgs a)
         // wholly past N, have nothing to add.
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {
-            const char *ks = smem + (t & 1) * Tr::STAGE;
-            const char *vs = ks + Tr::K_STAGE;
+            const char *kb = smem + (t & 1) * Tr::STAGE + k_rd;
+            const char *vb = smem + (t & 1) * Tr::STAGE + v_rd;
 
             f32x16_t sacc[Tr::JB];
 #pragma unroll
@@ -298,10 +318,8 @@ fa_fwd_kernel(FwdArgs a)
             for (int kk = 0; kk < Tr::DK; ++kk) {
 #pragma unroll
                 for (int jb = 0; jb < Tr::JB; ++jb) {
-                    const int row = jb * 32 + l32;
-                    const int ch = kk * 2 + h2;
                     const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
-                        ks + row * (D * 2) + ((ch ^ (row & Tr::K_SWZ)) << 4));
+                        kb + jb * 32 * Tr::K_PITCH + kk * 32);
                     sacc[jb] = M::run(kf, qf[kk], sacc[jb]);
                 }
             }
@@ -362,13 +380,10 @@ fa_fwd_kernel(FwdArgs a)
 
 #pragma unroll
             for (int nb = 0; nb < Tr::NB; ++nb) {
-                const int n = nb * 32 + l32;
-                const char *vrow = vs + n * (BC * 2);
-                const int sw = vt_swz(n, Tr::V_SWZ);
 #pragma unroll
                 for (int kstep = 0; kstep < Tr::KS; ++kstep) {
                     const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(
-                        vrow + (((2 * kstep + h2) ^ sw) << 4));
+                        vb + nb * 32 * Tr::V_PITCH + kstep * 32);
                     oacc[nb] = M::run(vf, pf[kstep], oacc[nb]);
                 }
             }
@@ -439,13 +454,13 @@ fa_fwd_f32_kernel(FwdArgs a)
     float *vl = kl + Tr::K_FLOATS;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
 
     int bh, qt;
-    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, CAUSAL, bh, qt);
+    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, a.B * a.Hq, CAUSAL, bh, qt);
     const int b = bh / a.Hq;
     const int hk = (bh - b * a.Hq) / a.group;
     const int N = a.N;

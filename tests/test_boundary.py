@@ -50,14 +50,14 @@ def check(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE 
 
 def test_valid_call_plans_a_launch():
     rc, p = check(B_=1, Hq=32, Hkv=32, N=4096, d=128)
-    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 64, 4, 1024)
-    assert p.lds_bytes == 2 * 2 * 64 * 128 * 2
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 32, 4, 1024)
+    assert p.lds_bytes == 2 * (32 * (2 * 128 + 16) + 128 * (2 * 32 + 16))
     rc, p = check(B_=4, Hq=32, Hkv=8, N=8192)
-    assert rc == 0 and p.grid == 4 * 32 * 64
+    assert rc == 0 and (p.br, p.bc, p.grid) == (256, 64, 4 * 32 * 32)
     rc, p = check(B_=1, Hq=1, Hkv=1, N=128, d=64, dt=F.F32, tuning=(32, 32))
     assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
     rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
-    assert rc == 0 and (p.br, p.bc) == (128, 32)
+    assert rc == 0 and (p.br, p.bc) == (128, 64)
     rc, p = check(lse=None)
     assert rc == 0
 
