@@ -13,9 +13,13 @@
 
 namespace fa355 {
 
-// LDS bytes of a 16-bit-input kernel: two stages of a K block (BC rows of 2D bytes)
-// and a transposed V block (D rows of 2BC bytes), every row padded by 16 bytes.
-constexpr int fwd_lds_bytes(int D, int BC) { return 2 * (BC * (2 * D + 16) + D * (2 * BC + 16)); }
+// LDS bytes of a 16-bit-input kernel: two stages, each a K block (BC rows of D
+// values plus one 16-byte pad per row) and a V block (plus two pads per row), each
+// rounded up to whole 1 KB DMA instructions.
+constexpr int fwd_lds_bytes(int D, int BC)
+{
+    return 2 * 16 * ((BC * (D / 8 + 1) + 63) / 64 * 64 + (BC * (D / 8 + 2) + 63) / 64 * 64);
+}
 
 struct FwdArgs {
     const void *q, *k, *v;

@@ -100,6 +100,31 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int byte_off
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L's data lands at
+// lds + 16 L (lds is wave-uniform).  Out-of-range lanes write zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)   // LDS pointers exist only in the device pass
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+#else
+    (void)r; (void)lds; (void)voff;
+#endif
+}
+
+// ds_read_b64_tr_b16: each group of 16 lanes reads a 4-row x 16-column block of
+// 16-bit values (lane L addresses 8 bytes of row (L % 16) / 4); lane L receives
+// the four values of column L % 16, rows 0..3 in order.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t read_tr16(const char *p) {
+#if defined(__HIP_DEVICE_COMPILE__)   // a gfx950 instruction: the host pass only sees a stub
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+#else
+    (void)p;
+    return u32x2_t{};
+#endif
+}
+
 // Values of lanes L and L^32 (same query row), in a fixed order on both lanes.
 __device__ __forceinline__ f32x2_t row_pair(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -147,18 +172,22 @@ struct FwdTraits {
     static constexpr int JB = BC / 32;           // 32-row blocks of the score tile
     static constexpr int KS = BC / 16;           // 16-key steps of P V
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-    static constexpr int RG = BC / 4;            // 4-row groups per V block
-    static constexpr int K_TOTAL = BC * CPR;     // 16-byte K chunks per block
-    static constexpr int V_TOTAL = RG * CPR;     // (4 rows x 1 chunk) V units per block
-    static constexpr int K_LOADS = (K_TOTAL + NT - 1) / NT;
-    static constexpr int V_UNITS = (V_TOTAL + NT - 1) / NT;
-    // LDS rows are padded by 16 bytes: consecutive rows then start 4 banks apart,
-    // so the 16-byte reads of 8 (or 16) consecutive rows hit distinct banks, and
-    // every read address is one per-lane base plus a compile-time offset.
-    static constexpr int K_PITCH = D * 2 + 16;   // K row j: D keys' worth of bytes
-    static constexpr int V_PITCH = BC * 2 + 16;  // V^T row n: BC keys
-    static constexpr int K_STAGE = BC * K_PITCH;
-    static constexpr int V_STAGE = D * V_PITCH;
+    // K and V blocks go from global memory straight into LDS (no registers).
+    // One 64-lane DMA instruction fills 64 consecutive 16-byte LDS slots, so a
+    // block is laid out in slots: K row j takes CPR slots plus one pad slot
+    // (rows start 4 banks apart: the 16-byte fragment reads of 8 consecutive rows
+    // hit distinct banks); V row j takes CPR slots plus two pad slots (rows start
+    // 8 banks apart: the four rows one transposed read touches hit distinct banks).
+    // Pad slots, and slots past the block, receive out-of-range (zero) loads.
+    static constexpr int K_PITCH = D * 2 + 16;
+    static constexpr int V_PITCH = D * 2 + 32;
+    static constexpr int K_SLOTS = (BC * (CPR + 1) + 63) / 64 * 64;
+    static constexpr int V_SLOTS = (BC * (CPR + 2) + 63) / 64 * 64;
+    static constexpr int K_INSTR = K_SLOTS / 64;
+    static constexpr int N_INSTR = (K_SLOTS + V_SLOTS) / 64;   // DMA instructions per block
+    static constexpr int P_INSTR = (N_INSTR + WAVES - 1) / WAVES;  // per wavefront
+    static constexpr int K_STAGE = K_SLOTS * 16;
+    static constexpr int V_STAGE = V_SLOTS * 16;
     static constexpr int STAGE = K_STAGE + V_STAGE;
     static constexpr int LDS = 2 * STAGE;
     static_assert(LDS == fwd_lds_bytes(D, BC), "LDS size");
@@ -166,7 +195,6 @@ struct FwdTraits {
     // matrix work; head dim 256 needs the whole register file for one.
     static constexpr int OCC = (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-    static_assert(NT % RG == 0, "V load split");
 };
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
@@ -213,77 +241,42 @@ fa_fwd_kernel(FwdArgs a)
     const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
     const int n_kv = (kv_len + BC - 1) / BC;
 
-    // Global -> register staging of the next block.  K: 16 consecutive lanes read
-    // one 256-byte row.  V: thread (4-row group rg, 16-byte column chunk cc), rg
-    // fastest, so that its transposed LDS writes from 16 lanes fill one V^T row.
-    const int k_row0 = tid / Tr::CPR, k_cc = tid % Tr::CPR;
-    const int v_rg = tid % Tr::RG, v_cc0 = tid / Tr::RG;
-    const int k_voff = k_row0 * ROW + k_cc * 16;
-    const int v_voff = 4 * v_rg * ROW + v_cc0 * 16;
-    u32x4_t kst[Tr::K_LOADS];
-    u32x4_t vst[Tr::V_UNITS][4];
+    // Per-lane source offsets of this wavefront's DMA instructions (loop-invariant):
+    // instruction i = p * WAVES + wave fills slots 64 i .. 64 i + 63 of the stage.
+    int dma_off[Tr::P_INSTR];
+#pragma unroll
+    for (int p = 0; p < Tr::P_INSTR; ++p) {
+        const int i = p * WAVES + wave;
+        const bool isk = i < Tr::K_INSTR;
+        const int slot = (isk ? i : i - Tr::K_INSTR) * 64 + lane;
+        const int spr = isk ? Tr::CPR + 1 : Tr::CPR + 2;     // slots per row
+        const int row = slot / spr, ch = slot - row * spr;
+        dma_off[p] = (row < BC && ch < Tr::CPR) ? row * ROW + ch * 16 : 0x7ffffff0;
+    }
 
-    auto load_block = [&](int t) {
-        // The block's rows start the buffer, so rows past N read as zero.
+    // Block t of K and V into LDS stage `stage`.  The block's rows start each
+    // buffer resource, so rows past N read as zero.
+    auto dma_block = [&](int t, int stage) {
         const int j0 = t * BC;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)j0 * ROW, (N - j0) * ROW);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)j0 * ROW, (N - j0) * ROW);
+        char *st = smem + stage * Tr::STAGE;
 #pragma unroll
-        for (int c = 0; c < Tr::K_LOADS; ++c) {
-            if (Tr::K_TOTAL % Tr::NT != 0 && c * Tr::NT + tid >= Tr::K_TOTAL)
+        for (int p = 0; p < Tr::P_INSTR; ++p) {
+            const int i = p * WAVES + wave;
+            if (Tr::N_INSTR % WAVES != 0 && i >= Tr::N_INSTR)
                 break;
-            kst[c] = load16(rk, k_voff + c * (Tr::NT / Tr::CPR) * ROW);
-        }
-#pragma unroll
-        for (int u = 0; u < Tr::V_UNITS; ++u) {
-            if (Tr::V_TOTAL % Tr::NT != 0 && u * Tr::NT + tid >= Tr::V_TOTAL)
-                break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vst[u][e] = load16(rv, v_voff + e * ROW + u * (Tr::NT / Tr::RG) * 16);
+            dma16(i < Tr::K_INSTR ? rk : rv, st + i * 1024, dma_off[p]);
         }
     };
 
-    // LDS write addresses (per lane, loop-invariant).
-    const int k_wr = k_row0 * Tr::K_PITCH + k_cc * 16;
-    // V^T: keys 4rg..4rg+3 of output column n become 8 bytes of row n.  Within each
-    // 16-key group the 4-key groups are stored in the order 0, 2, 1, 3, so that the
-    // eight keys one lane feeds to one P.V step are one 16-byte chunk.
-    const int v_g4 = v_rg & 3;
-    const int v_wr = (v_cc0 * 8) * Tr::V_PITCH + (v_rg >> 2) * 32 + (v_g4 & 1) * 16 + (v_g4 >> 1) * 8;
-
-    auto store_block = [&](int stage) {
-        char *ks = smem + stage * Tr::STAGE;
-        char *vs = ks + Tr::K_STAGE;
-#pragma unroll
-        for (int c = 0; c < Tr::K_LOADS; ++c) {
-            if (Tr::K_TOTAL % Tr::NT != 0 && c * Tr::NT + tid >= Tr::K_TOTAL)
-                break;
-            *reinterpret_cast<u32x4_t *>(ks + k_wr + c * (Tr::NT / Tr::CPR) * Tr::K_PITCH) = kst[c];
-        }
-#pragma unroll
-        for (int u = 0; u < Tr::V_UNITS; ++u) {
-            if (Tr::V_TOTAL % Tr::NT != 0 && u * Tr::NT + tid >= Tr::V_TOTAL)
-                break;
-            char *vw = vs + v_wr + u * (Tr::NT / Tr::RG) * 8 * Tr::V_PITCH;
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {        // dword qd holds columns 2qd, 2qd+1
-                const uint32_t x0 = vst[u][0][qd], x1 = vst[u][1][qd];
-                const uint32_t x2 = vst[u][2][qd], x3 = vst[u][3][qd];
-                u32x2_t lo, hi;
-                lo[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-                lo[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-                hi[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-                hi[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-                *reinterpret_cast<u32x2_t *>(vw + (2 * qd) * Tr::V_PITCH) = lo;
-                *reinterpret_cast<u32x2_t *>(vw + (2 * qd + 1) * Tr::V_PITCH) = hi;
-            }
-        }
-    };
-
-    // LDS read bases (per lane): K row l32 chunk h2, V^T row l32 chunk h2.
+    // LDS read bases (per lane).  K: row l32, chunk h2 (16-byte reads).  V: the
+    // transposed 64-bit read gives each 16-lane group a 4-key x 16-column block,
+    // lane L receiving column L % 16 of it; lane L addresses key row
+    // 4 * (L / 32) + (L % 16) / 4 and columns 16 * ((L / 16) % 2) + 4 * (L % 4).
     const int k_rd = l32 * Tr::K_PITCH + h2 * 16;
-    const int v_rd = Tr::K_STAGE + l32 * Tr::V_PITCH + h2 * 16;
+    const int v_rd = Tr::K_STAGE + (4 * h2 + ((lane & 15) >> 2)) * Tr::V_PITCH +
+                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
     f32x16_t oacc[Tr::NB];
 #pragma unroll
@@ -294,14 +287,13 @@ fa_fwd_kernel(FwdArgs a)
     float le_part = 0.0f;      // fp32 sum of unrounded P, for lse (bf16 only)
     const float c = a.c;
 
-    load_block(0);
-    store_block(0);
+    dma_block(0, 0);
     __syncthreads();
 
     for (int t = 0; t < n_kv; ++t) {
         const int j0 = t * BC;
         if (t + 1 < n_kv)
-            load_block(t + 1);
+            dma_block(t + 1, (t + 1) & 1);
 
         // Blocks wholly above this wavefront's causal diagonal, and wavefronts
         // wholly past N, have nothing to add.
@@ -314,14 +306,25 @@ fa_fwd_kernel(FwdArgs a)
 #pragma unroll
             for (int jb = 0; jb < Tr::JB; ++jb)
                 sacc[jb] = f32x16_t{};
+            // K fragments are read in batches of up to eight ahead of their matrix
+            // instructions, so LDS latency overlaps the MFMA chain instead of
+            // stalling each instruction.
+            constexpr int KB = (8 / Tr::JB) < Tr::DK ? (8 / Tr::JB) : Tr::DK;   // kk per batch
 #pragma unroll
-            for (int kk = 0; kk < Tr::DK; ++kk) {
+            for (int k0 = 0; k0 < Tr::DK; k0 += KB) {
+                u32x4_t kf[KB][Tr::JB];
 #pragma unroll
-                for (int jb = 0; jb < Tr::JB; ++jb) {
-                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
-                        kb + jb * 32 * Tr::K_PITCH + kk * 32);
-                    sacc[jb] = M::run(kf, qf[kk], sacc[jb]);
-                }
+                for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                    for (int jb = 0; jb < Tr::JB; ++jb)
+                        kf[kk][jb] = *reinterpret_cast<const u32x4_t *>(
+                            kb + jb * 32 * Tr::K_PITCH + (k0 + kk) * 32);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                    for (int jb = 0; jb < Tr::JB; ++jb)
+                        sacc[jb] = M::run(kf[kk][jb], qf[k0 + kk], sacc[jb]);
             }
 
             if ((CAUSAL && j0 + BC - 1 > iw0) || j0 + BC > N) {
@@ -382,15 +385,16 @@ fa_fwd_kernel(FwdArgs a)
             for (int nb = 0; nb < Tr::NB; ++nb) {
 #pragma unroll
                 for (int kstep = 0; kstep < Tr::KS; ++kstep) {
-                    const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(
-                        vb + nb * 32 * Tr::V_PITCH + kstep * 32);
+                    // Keys 16 kstep + 4 (L/32) + 0..3 and the same + 8 of column n.
+                    const char *va = vb + kstep * 16 * Tr::V_PITCH + nb * 64;
+                    const u32x2_t lo = read_tr16(va), hi = read_tr16(va + 8 * Tr::V_PITCH);
+                    const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
                     oacc[nb] = M::run(vf, pf[kstep], oacc[nb]);
                 }
             }
         }
 
-        if (t + 1 < n_kv)
-            store_block((t + 1) & 1);
+        // The barrier's fence also waits for this iteration's DMA.
         __syncthreads();
     }
 
