@@ -11,7 +11,9 @@ value       = algorithmic FLOPs (4*B*Hq*N^2*d, halved when causal) * K / wall ti
               the K timed steps, bracketed by device synchronisation.
 roofline    = the kernel's own rate: FLOPs per launch / average launch duration from
               HIP events recorded on the launch stream around the timed region, against
-              the 2.5 PFLOP/s dense bf16 MFMA peak.  traffic = HBM bytes per launch from
+              the 2.5 PFLOP/s dense bf16 MFMA peak -- or, for a workload whose FLOPs per
+              compulsory byte fall below the ridge point, compulsory bytes / duration
+              against 8 TB/s of HBM.  traffic = HBM bytes per launch from
               rocprofv3 FETCH_SIZE / WRITE_SIZE counters, calibrated on a copy of known
               size (read from profiles/, null when the kernel sources changed since).
 cpu_baseline = the fp64 CPU oracle, as it stands, on a bounded sample of query rows of
@@ -34,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (causal, d=128, N=4096)"
 DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp")
 
@@ -170,8 +173,16 @@ def run(args) -> dict:
     flops = x.flops
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[x.dtype]
+    # Compulsory HBM bytes: Q, K, V read once; O and lse written once.  Below the
+    # ridge point (peak FLOP/s / peak bytes/s) the kernel is bounded by HBM.
+    nbytes = x.q.nbytes + x.k.nbytes + x.v.nbytes + x.q.nbytes + x.B * x.Hq * x.N * 4
+    peak_flops = PEAK_TFLOPS[x.dtype]
+    if flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
+        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    else:
+        bound, unit, peak = "mfma", "TFLOP/s", peak_flops
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -188,8 +199,8 @@ def run(args) -> dict:
         "config": {"workload": args.workload, "B": x.B, "Hq": x.Hq, "Hkv": x.Hkv, "N": x.N,
                    "d": x.d, "causal": x.causal, "scale": x.scale, "seed": x.seed,
                    "tile": [plan.br, plan.bc], "waves": plan.waves, "grid": plan.grid},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
