@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle of attention, forward and gradients -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` import this package.  The product library never does, and this
@@ -10,7 +10,9 @@ Two independent C implementations sit behind these wrappers:
 * ``attention`` / ``probs`` -- the plain definition softmax(Q K^T * scale) V with a
   two-pass softmax over materialised score rows (attention_oracle.c);
 * ``blocked`` -- the tiled online-softmax merge equations, key/value blocks outer,
-  query blocks inner, per-row state (blocked_reference.c).
+  query blocks inner, per-row state (blocked_reference.c);
+* ``grads`` -- dQ, dK, dV of the plain definition by the chain rule, one softmax
+  row at a time (attention_grad_oracle.c).
 
 Every function here is pinned by tests against things other than itself (high
 precision brute force, closed forms, invariants, torch's own attention routine).
@@ -24,7 +26,7 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ("attention_oracle.c", "blocked_reference.c")
+SOURCES = ("attention_oracle.c", "blocked_reference.c", "attention_grad_oracle.c")
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 CFLAGS = ("-O2", "-std=gnu11", "-fPIC", "-shared", "-pthread")
 
@@ -53,6 +55,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blocked_attention_fwd.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                           ip, ctypes.c_double, i64, i64]
     lib.blocked_attention_fwd.restype = ip
+    lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                         ip, ctypes.c_double, ip]
+    lib.oracle_attention_bwd.restype = ip
     return lib
 
 
@@ -131,3 +136,24 @@ def blocked(q, k, v, causal: bool, scale: float, br: int, bc: int, lib=None):
     if rc != 0:
         raise ValueError(f"blocked_attention_fwd failed with {rc}")
     return o, lse
+
+
+def grads(q, k, v, dout, causal: bool, scale: float, threads: int = 0, lib=None):
+    """Gradients of sum(O * dout) for O = attention(q, k, v): returns (dq, dk, dv).
+
+    q, dout: [B,Hq,N,d]; k, v: [B,Hkv,N,d]; outputs have the shapes of q, k, v.
+    """
+    L = _get(lib)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError(f"dout shape {dout.shape} != q shape {q.shape}")
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = L.oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_bwd failed with {rc}")
+    return dq, dk, dv

@@ -11,9 +11,11 @@ import pytest
 
 import oracle
 import oracle_pins as P
+import grad_pins as GP
 
 ORACLE = "attention_oracle.c"
 BLOCKED = "blocked_reference.c"
+GRAD = "attention_grad_oracle.c"
 
 # (id, file, [(original, replacement), ...])
 MUTANTS = [
@@ -41,6 +43,15 @@ MUTANTS = [
     ("blocked_local_max_ignored", BLOCKED, [("const double p = exp(sblk[j - j0] - mt);",
                                              "const double p = exp(sblk[j - j0] - mn_unused);"),
                                             ("double lt = 0.0;", "double lt = 0.0; const double mn_unused = (m[i] > mt) ? m[i] : mt;")]),
+    ("grad_no_row_term", GRAD, [("const double ds = p[j] * (dp[j] - pdp);", "const double ds = p[j] * dp[j];")]),
+    ("grad_dk_unscaled", GRAD, [("dkh[j * d + t] += J->scale * ds * qi[t];", "dkh[j * d + t] += ds * qi[t];")]),
+    ("grad_dq_from_v", GRAD, [("dqi[t] += J->scale * ds * kh[j * d + t];", "dqi[t] += J->scale * ds * vh[j * d + t];")]),
+    ("grad_dv_uses_ds", GRAD, [("dvh[j * d + t] += p[j] * gi[t];", "dvh[j * d + t] += ds * gi[t];")]),
+    ("grad_causal_strict", GRAD, [("const int64_t jend = J->causal ? i + 1 : N;", "const int64_t jend = J->causal ? i : N;")]),
+    ("grad_dp_from_q", GRAD, [("acc += gi[t] * vh[j * d + t];", "acc += gi[t] * kh[j * d + t];")]),
+    ("grad_gqa_first_head_only", GRAD, [("for (int64_t h = hk * G; h < (hk + 1) * G; ++h) {",
+                                         "for (int64_t h = hk * G; h < hk * G + 1; ++h) {")]),
+    ("grad_row_term_unweighted", GRAD, [("pdp += p[j] * acc;", "pdp += acc;")]),
 ]
 
 
@@ -49,6 +60,12 @@ def _quick_oracle_pins(lib):
     P.pin_torch_sdpa(lib)
     P.pin_closed_forms(lib)
     P.pin_invariants(lib)
+
+
+def _quick_grad_pins(lib):
+    GP.pin_grad_closed_forms(lib)
+    GP.pin_grad_invariants(lib)
+    GP.pin_grad_finite_differences(lib, quick=True)
 
 
 def _build_mutant(tmp_path, fname, edits):
@@ -69,6 +86,11 @@ def _build_mutant(tmp_path, fname, edits):
 @pytest.mark.parametrize("mid,fname,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, mid, fname, edits):
     lib = _build_mutant(tmp_path, fname, edits)
-    pins = _quick_oracle_pins if fname == ORACLE else (lambda L: P.pin_blocked_agrees(L, quick=True))
+    if fname == ORACLE:
+        pins = _quick_oracle_pins
+    elif fname == GRAD:
+        pins = _quick_grad_pins
+    else:
+        pins = lambda L: P.pin_blocked_agrees(L, quick=True)
     with pytest.raises(AssertionError):
         pins(lib)
