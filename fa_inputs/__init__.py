@@ -244,6 +244,15 @@ def make_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str
                            int(seed), out[0], out[1], out[2], recipe, extra)
 
 
+def make_grad_output(seed: int, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
+    """A seeded upstream gradient dL/dO: N(0,1) draws (times mult), rounded, as storage."""
+    st = Stream(seed)
+    g = st.normals(int(np.prod(shape))).reshape(shape)
+    if mult != 1.0:
+        g *= mult
+    return to_storage(round_to_dtype(g, dtype), dtype)
+
+
 # The six measured workloads.  Shapes follow the pages' layers: a 4096-token
 # Llama-7B layer (32 heads of 128), BERT-large at sequence 512, 32/8 grouped-query
 # heads, and long contexts with inputs scaled by 3 to exercise the rescaling.

@@ -115,6 +115,32 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
                  float scale, fa355_dtype in_dtype, fa355_dtype o_dtype,
                  const fa355_tuning *tuning, fa355_plan *plan);
 
+/*
+ * Backward pass: the gradients of sum(O * dout) for O = fa_fwd(q, k, v), i.e. of
+ * any loss L with dL/dO = dout ("FlashAttention (VI)", equation Attention,
+ * differentiated; the forward pass keeps no N x N matrix for it, as the Ascend
+ * page's section on standard attention's memory asks -- P is recomputed from lse).
+ *   q, k, v    the forward inputs (layouts above), element type `dtype`
+ *   o          the forward output [B,Hq,N,d], element type `dtype`
+ *   dout       dL/dO [B,Hq,N,d], element type `dtype`
+ *   lse        the forward pass's logsumexp [B,Hq,N] fp32 (natural log, scaled units)
+ *   dq         device pointer [B,Hq,N,d] fp32; written with dL/dQ
+ *   dk, dv     device pointers [B,Hkv,N,d] fp32; written with dL/dK and dL/dV (for
+ *              grouped-query attention, summed over the query heads of each K/V head)
+ *   delta      device pointer [B,Hq,N] fp32, a caller-owned workspace; on return it
+ *              holds D_i = dout_i . o_i
+ *   B .. scale as for fa_fwd (the same scale and causal flag as the forward call);
+ *              dtype F16 or BF16, d in {64, 128}
+ * All of q, k, v, o, dout, dq, dk, dv must be 16-byte aligned, lse and delta 4-byte
+ * aligned; none of dq, dk, dv, delta may overlap each other or any input.
+ * Enqueues three kernels on `stream` and returns; allocates nothing.  Errors as for
+ * fa_fwd: validation runs before any HIP call and leaves the outputs untouched.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, float *dq, float *dk, float *dv, float *delta,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           fa355_dtype dtype, hipStream_t stream);
+
 /* A static, human-readable name for a status code ("unknown status" otherwise). */
 const char *fa_status_str(int status);
 

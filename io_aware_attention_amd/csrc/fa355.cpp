@@ -188,6 +188,95 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse,
     return c.var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
 }
 
+using BwdLaunchFn = hipError_t (*)(const fa355::BwdArgs &, hipStream_t);
+
+struct BwdVariant {
+    int dtype;
+    int d;
+    bool causal;
+    BwdLaunchFn fn;
+};
+
+#define FA355_BWD_ROW(T, D, C) {FA355_DT_##T, D, C, &fa355::launch_bwd<fa355::T, D, C>},
+const BwdVariant kBwdVariants[] = {
+    FA355_BWD_VARIANTS(FA355_BWD_ROW, BF16)
+    FA355_BWD_VARIANTS(FA355_BWD_ROW, F16)
+};
+
+constexpr int kBwdTile = 128;   // query rows per dQ workgroup, keys per dK/dV workgroup
+
+int run_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+            const float *lse, float *dq, float *dk, float *dv, float *delta,
+            int B, int Hq, int Hkv, int N, int d, int causal, float scale, int dt,
+            hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
+        return FA355_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+    if ((dt != FA355_F16 && dt != FA355_BF16) || (d != 64 && d != 128))
+        return FA355_ERR_UNSUPPORTED;
+    // One head (16-bit inputs, fp32 gradients) must fit 32-bit byte offsets.
+    if ((int64_t)N * d * 4 > INT_MAX - 65536)
+        return FA355_ERR_SHAPE;
+    if (!std::isfinite(scale))
+        return FA355_ERR_ARG;
+    const void *al16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void *p : al16)
+        if (reinterpret_cast<uintptr_t>(p) % 16)
+            return FA355_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(delta) % 4)
+        return FA355_ERR_ALIGN;
+    const size_t nq = (size_t)B * Hq * N * d, nkv = (size_t)B * Hkv * N * d, nr = (size_t)B * Hq * N;
+    struct Span { const void *p; size_t n; };
+    const Span in[] = {{q, nq * 2}, {k, nkv * 2}, {v, nkv * 2}, {o, nq * 2}, {dout, nq * 2}, {lse, nr * 4}};
+    const Span out[] = {{dq, nq * 4}, {dk, nkv * 4}, {dv, nkv * 4}, {delta, nr * 4}};
+    for (size_t x = 0; x < 4; ++x) {
+        for (const Span &i : in)
+            if (overlaps(out[x].p, out[x].n, i.p, i.n))
+                return FA355_ERR_ARG;
+        for (size_t y = x + 1; y < 4; ++y)
+            if (overlaps(out[x].p, out[x].n, out[y].p, out[y].n))
+                return FA355_ERR_ARG;
+    }
+    const BwdVariant *var = nullptr;
+    for (const BwdVariant &x : kBwdVariants)
+        if (x.dtype == dt && x.d == d && x.causal == (causal != 0))
+            var = &x;
+    if (!var)
+        return FA355_ERR_UNSUPPORTED;
+    const int64_t n_tiles = (N + kBwdTile - 1) / kBwdTile;
+    if ((int64_t)B * Hq * n_tiles > INT_MAX || (int64_t)B * Hq * N > INT_MAX)
+        return FA355_ERR_SHAPE;
+
+    fa355::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.group = Hq / Hkv;
+    a.n_qtiles = (int)n_tiles;
+    a.total_tiles = (int)(B * Hq * n_tiles);
+    a.n_ktiles = (int)n_tiles;
+    float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+    if (!(c >= 1.17549435e-38f))
+        c = 1.17549435e-38f;
+    a.c = c;
+    a.scale = scale;
+    a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    return var->fn(a, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -235,6 +324,15 @@ const char *fa_status_str(int status)
     }
 }
 
-int fa_version(void) { return 100; }
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, float *dq, float *dk, float *dv, float *delta,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           fa355_dtype dtype, hipStream_t stream)
+{
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
+                   dtype, stream);
+}
+
+int fa_version(void) { return 110; }
 
 }  // extern "C"

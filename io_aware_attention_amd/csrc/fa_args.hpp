@@ -33,6 +33,22 @@ struct FwdArgs {
     uint32_t q_sign;   // 0x80008000 flips the sign of every 16-bit Q element
 };
 
+// Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;   // [B,Hq,N] from the forward pass (natural log, scaled units)
+    float *delta;       // [B,Hq,N] workspace: D_i = dO_i . O_i
+    float *dq, *dk, *dv;
+    int B, Hq, Hkv, N;
+    int group;          // Hq / Hkv
+    int n_qtiles;       // ceil(N / 128): query tiles of the dQ kernel
+    int total_tiles;    // B * Hq * n_qtiles
+    int n_ktiles;       // ceil(N / 128): key tiles of the dK/dV kernel
+    float c;            // |scale| * log2(e), FLT_MIN for a zero scale
+    float scale;        // the signed scale, applied to dQ and dK
+    uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q, or K, in the scores)
+};
+
 struct BF16 {};
 struct F16 {};
 
@@ -42,6 +58,10 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+
+// The three backward kernels (delta, dK/dV, dQ), in order on `stream`.
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
 }  // namespace fa355
 
@@ -64,3 +84,6 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
     X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)
 
 #define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
+
+// Backward variants: Z(T, D, CAUSAL), 16-bit inputs, head dims 64 and 128.
+#define FA355_BWD_VARIANTS(Z, T) Z(T, 64, false) Z(T, 64, true) Z(T, 128, false) Z(T, 128, true)

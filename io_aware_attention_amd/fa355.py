@@ -1,6 +1,7 @@
 """ctypes binding of libfa355 -- argument marshalling only.
 
-Every step of the attention forward pass runs in the library's HIP kernels; this
+Every step of the attention forward and backward passes runs in the library's HIP
+kernels; this
 module only turns torch tensors into pointers, sizes and a stream, and turns
 status codes into exceptions.  torch provides device memory and streams.  If the
 built library is missing, importing the binding's functions raises: there is no
@@ -19,7 +20,7 @@ F32, F16, BF16 = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 
 # Every exported symbol, as declared in include/fa355.h.
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_bwd", "fa_status_str", "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_ex.restype = ip
     L.fa_fwd_check.argtypes = common + [ip, ip, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
     L.fa_fwd_check.restype = ip
+    L.fa_bwd.argtypes = [vp] * 10 + [ip, ip, ip, ip, ip, ip, fp, ip, vp]
+    L.fa_bwd.restype = ip
     L.fa_status_str.argtypes = [ip]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -149,3 +152,47 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out_dtype=
                      _tuning(tuning), ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, *,
+        dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Attention backward on torch device tensors: returns (dq, dk, dv), fp32.
+
+    q, o, dout: [B,Hq,N,d]; k, v: [B,Hkv,N,d]; all contiguous, one 16-bit dtype.
+    lse: [B,Hq,N] fp32 from the forward pass with the same causal flag and scale.
+    dq / dk / dv / delta (the [B,Hq,N] fp32 workspace) may be preallocated.
+    """
+    import torch
+    L = lib()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if tuple(t.shape) != tuple(shape) or t.dtype != q.dtype:
+            raise FA355Error(ERR_SHAPE, f"{name} must match q in shape and dtype")
+    if tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
+        raise FA355Error(ERR_SHAPE, "lse must be fp32 [B,Hq,N]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, Hq, N, d), **f32) if dq is None else dq
+    dk = torch.empty((B, Hkv, N, d), **f32) if dk is None else dk
+    dv = torch.empty((B, Hkv, N, d), **f32) if dv is None else dv
+    delta = torch.empty((B, Hq, N), **f32) if delta is None else delta
+    for name, t, shape in (("dq", dq, (B, Hq, N, d)), ("dk", dk, (B, Hkv, N, d)),
+                           ("dv", dv, (B, Hkv, N, d)), ("delta", delta, (B, Hq, N))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} has the wrong shape, dtype or layout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                  B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _dtype_code(q.dtype),
+                  ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return dq, dk, dv

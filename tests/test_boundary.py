@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = F.lib()
-    assert L.fa_version() == 100
+    assert L.fa_version() == 110
     for s in range(-6, 1):
         assert F.status_str(s) and F.status_str(s) != "unknown status"
     assert F.status_str(-99) == "unknown status"
@@ -104,3 +104,24 @@ def test_python_plan_helper():
     assert p.grid == 16 * 16 * 4
     with pytest.raises(F.FA355Error):
         F.plan(1, 1, 1, 8, 80, False, torch.bfloat16)
+
+
+def bwd_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, do=BASE + 4 * SPAN,
+             lse=BASE + 5 * SPAN, dq=BASE + 6 * SPAN, dk=BASE + 7 * SPAN, dv=BASE + 8 * SPAN,
+             delta=BASE + 9 * SPAN, B_=1, Hq=4, Hkv=2, N=100, d=128, causal=1, scale=0.1,
+             dt=F.BF16):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, B_, Hq, Hkv, N, d, causal,
+                          scale, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(do=None), -1), (dict(lse=None), -1), (dict(delta=None), -1),
+    (dict(dq=None), -1), (dict(B_=0), -2), (dict(Hq=3, Hkv=2), -2), (dict(N=0), -2),
+    (dict(d=256), -3), (dict(d=96), -3), (dict(dt=F.F32, d=64), -3), (dict(dt=9), -3),
+    (dict(scale=float("nan")), -5), (dict(q=BASE + 8), -4), (dict(dk=BASE + 7 * SPAN + 4), -4),
+    (dict(lse=BASE + 5 * SPAN + 2), -4), (dict(dq=BASE), -5), (dict(dv=BASE + 7 * SPAN + 64), -5),
+    (dict(delta=BASE + 4 * SPAN + 128), -5), (dict(dk=BASE + 6 * SPAN + 4096), -5),
+])
+def test_bwd_rejections(kw, code):
+    assert bwd_call(**kw) == code, kw
