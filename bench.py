@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --profile-run      # a few launches + a calibration copy, for rocprofv3
+    python bench.py --bwd [...]        # the backward pass (fa_bwd) on the same workload
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
 batch of seeded synthetic inputs already resident in device memory.  The default
@@ -34,6 +35,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (causal, d=128, N=4096)"
+METRIC_BWD = "attention bwd TFLOP/s and % of MI355X bf16 MFMA peak"
+BWD_FLOP_RATIO = 2.5   # backward = 5 matrix products (S, dP, dV, dK, dQ) vs the forward's 2
 DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -123,6 +126,33 @@ def cpu_baseline(x, budget_s: float = 15.0) -> dict:
             "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads"}
 
 
+def cpu_baseline_bwd(x, budget_s: float) -> dict:
+    """The fp64 gradient oracle, as it stands, on whole heads of the workload."""
+    import oracle
+
+    threads = os.cpu_count() or 1
+    G = x.Hq // x.Hkv
+    # Gradient units are whole K/V groups; take as many as there are threads.
+    groups = max(1, min(x.Hkv, threads))
+    nh = groups * G
+
+    def f64(name, h0, h1):
+        from fa_inputs import storage_to_f64
+        return storage_to_f64(getattr(x, name)[0:1, h0:h1], x.dtype)
+
+    import fa_inputs
+    g = fa_inputs.storage_to_f64(fa_inputs.make_grad_output(4242, (1, nh, x.N, x.d), x.dtype), x.dtype)
+    t0 = time.perf_counter()
+    oracle.grads(f64("q", 0, nh), f64("k", 0, groups), f64("v", 0, groups), g, x.causal, x.scale,
+                 threads=threads)
+    dt = time.perf_counter() - t0
+    flops = BWD_FLOP_RATIO * x.flops / (x.B * x.Hq) * nh
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, groups),
+            "kind": "oracle",
+            "sample": f"all {x.N} rows of heads 0..{nh - 1} (batch 0) of {x.recipe}, gradients; "
+                      f"{dt:.1f} s in fp64 on {min(threads, groups)} threads"}
+
+
 def run(args) -> dict:
     import torch
 
@@ -142,6 +172,21 @@ def run(args) -> dict:
 
     def step():
         F.fwd(q, k, v, causal=x.causal, scale=x.scale, o=o, lse=lse, tuning=tuning, stream=stream)
+
+    if args.bwd:
+        # The backward pass over the forward pass's own O and lse.
+        step()
+        dout = torch.from_numpy(G.make_grad_output(4242, (x.B, x.Hq, x.N, x.d), x.dtype))
+        dout = (dout.view(torch.bfloat16) if x.dtype == "bf16" else dout).to(dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        dq = torch.empty((x.B, x.Hq, x.N, x.d), **f32)
+        dk = torch.empty((x.B, x.Hkv, x.N, x.d), **f32)
+        dv = torch.empty((x.B, x.Hkv, x.N, x.d), **f32)
+        delta = torch.empty((x.B, x.Hq, x.N), **f32)
+
+        def step():  # noqa: F811
+            F.bwd(q, k, v, o, dout, lse, causal=x.causal, scale=x.scale, dq=dq, dk=dk, dv=dv,
+                  delta=delta, stream=stream)
 
     if args.profile_run:
         for _ in range(3):
@@ -170,21 +215,21 @@ def run(args) -> dict:
     if not torch.isfinite(o.float()).all():
         raise RuntimeError("non-finite output")
 
-    flops = x.flops
+    flops = x.flops * (BWD_FLOP_RATIO if args.bwd else 1.0)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Compulsory HBM bytes: Q, K, V read once; O and lse written once.  Below the
     # ridge point (peak FLOP/s / peak bytes/s) the kernel is bounded by HBM.
     nbytes = x.q.nbytes + x.k.nbytes + x.v.nbytes + x.q.nbytes + x.B * x.Hq * x.N * 4
     peak_flops = PEAK_TFLOPS[x.dtype]
-    if flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
+    if not args.bwd and flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
         bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
         achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     else:
         bound, unit, peak = "mfma", "TFLOP/s", peak_flops
         achieved = flops / (kernel_ms * 1e-3) / 1e12
     line = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -201,11 +246,15 @@ def run(args) -> dict:
                    "tile": [plan.br, plan.bc], "waves": plan.waves, "grid": plan.grid},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": load_traffic(args.workload),
+                     "traffic": None if args.bwd else load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if args.bwd:
+        line["config"]["pass"] = "backward (fa_bwd: delta, dK/dV, dQ kernels)"
+        line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        line["cpu_baseline"] = (cpu_baseline_bwd(x, args.cpu_seconds) if args.bwd
+                                else cpu_baseline(x, args.cpu_seconds))
     return line
 
 
@@ -218,6 +267,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (fa_bwd) instead; FLOPs = 2.5x the forward's")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the forward pass of one device's share is "

@@ -172,10 +172,11 @@ fa_bwd_dkdv_kernel(BwdArgs a)
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
 
-    // Longest key tiles first when causal (they see the most queries).
-    const int n_kt = a.n_ktiles;
-    const int bhk = blockIdx.x / n_kt;
-    const int kt = CAUSAL ? n_kt - 1 - (blockIdx.x % n_kt) : blockIdx.x % n_kt;
+    // Key tile major: every head's first key tile, then every head's second, ...
+    // With causal masking the first tiles see the most queries, so the longest
+    // workgroups start first and the short ones fill the end of the launch.
+    const int kt = blockIdx.x / (a.B * a.Hkv);
+    const int bhk = blockIdx.x - kt * (a.B * a.Hkv);
     const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
     const int N = a.N;
     const int j0w = kt * Tr::BK + wave * 32;   // this wavefront's first key
@@ -242,7 +243,9 @@ fa_bwd_dkdv_kernel(BwdArgs a)
                 s = M::run(qa, kf[kk], s);
                 dp = M::run(ga, vf[kk], dp);
             }
-            // Register r of lane L is query i0 + 8(r/4) + 4 h2 + r%4, key jk.
+            // Register r of lane L is query i0 + 8(r/4) + 4 h2 + r%4, key jk.  Only
+            // blocks on the causal diagonal or past N need the visibility test.
+            const bool edge = (CAUSAL && i0 < j0w + 31) || i0 + 32 > N || j0w + 32 > N;
             float p[16], ds[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -251,9 +254,12 @@ fa_bwd_dkdv_kernel(BwdArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    const int qi = i0 + 8 * g + 4 * h2 + e;
-                    const bool vis = qi < N && jk < N && (!CAUSAL || jk <= qi);
-                    p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse4[e] * kLog2e)) : 0.0f;
+                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse4[e] * kLog2e));
+                    if (edge) {
+                        const int qi = i0 + 8 * g + 4 * h2 + e;
+                        const bool vis = qi < N && jk < N && (!CAUSAL || jk <= qi);
+                        p[r] = vis ? p[r] : 0.0f;
+                    }
                     ds[r] = p[r] * (dp[r] - dl4[e]);
                 }
             }
@@ -269,7 +275,7 @@ fa_bwd_dkdv_kernel(BwdArgs a)
                     dk[nb] = M::run(tr_frag<QL::PITCH>(qb, lane, nb, ks), pd[ks], dk[nb]);
                 }
         }
-        __syncthreads();
+        __syncthreads();      // its fence also waits for the next block's DMA
     };
     for (int u = 0; u < steps; u += 2) {
         step(Parity<0>{}, u);
@@ -390,13 +396,18 @@ fa_bwd_dq_kernel(BwdArgs a)
                 s = M::run(ka, qf[kk], s);
                 dp = M::run(va, gf[kk], dp);
             }
-            // Register r of lane L is key j0 + 8(r/4) + 4 h2 + r%4, query iq.
+            // Register r of lane L is key j0 + 8(r/4) + 4 h2 + r%4, query iq.  Only
+            // blocks on the causal diagonal or past N need the visibility test.
+            const bool edge = (CAUSAL && j0 + 31 > iw0) || j0 + 32 > N;
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                const bool vis = j < N && (!CAUSAL || j <= iq);
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) : 0.0f;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+                if (edge) {
+                    const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    const bool vis = j < N && (!CAUSAL || j <= iq);
+                    p = vis ? p : 0.0f;
+                }
                 ds[r] = p * (dp[r] - dl);
             }
             u32x4_t pd[2];
