@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --profile-run      # a few launches + a calibration copy, for rocprofv3
     python bench.py --bwd [...]        # the backward pass (fa_bwd) on the same workload
+    python bench.py --split [S] [...]  # the split-KV forward (fa_fwd_split)
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
 batch of seeded synthetic inputs already resident in device memory.  The default
@@ -173,6 +174,16 @@ def run(args) -> dict:
     def step():
         F.fwd(q, k, v, causal=x.causal, scale=x.scale, o=o, lse=lse, tuning=tuning, stream=stream)
 
+    if args.split is not None:
+        S = args.split or F.split_count(x.B, x.Hq, x.N, x.causal)
+        f32 = dict(dtype=torch.float32, device=dev)
+        o_part = torch.empty((S, x.B, x.Hq, x.N, x.d), **f32)
+        lse_part = torch.empty((S, x.B, x.Hq, x.N), **f32)
+
+        def step():  # noqa: F811
+            F.fwd_split(q, k, v, causal=x.causal, scale=x.scale, num_splits=S, o=o, lse=lse,
+                        o_part=o_part, lse_part=lse_part, stream=stream)
+
     if args.bwd:
         # The backward pass over the forward pass's own O and lse.
         step()
@@ -249,6 +260,10 @@ def run(args) -> dict:
                      "traffic": None if args.bwd else load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if args.split is not None:
+        line["config"]["pass"] = f"split-KV forward (fa_fwd_split, {S} splits: partials + merge)"
+        line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
+        line["roofline"]["traffic"] = None
     if args.bwd:
         line["config"]["pass"] = "backward (fa_bwd: delta, dK/dV, dQ kernels)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
@@ -267,6 +282,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--split", type=int, nargs="?", const=0, default=None,
+                    help="time the split-KV forward (fa_fwd_split) with this many splits "
+                         "(no value: the binding's split_count)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) instead; FLOPs = 2.5x the forward's")
     args = ap.parse_args(argv)

@@ -270,6 +270,9 @@ WORKLOADS = {
                                            d=128, dtype="bf16", causal=True, mult=3.0),
     "bf16_h8_n8192_d256_causal_x3": dict(seed=1006, B=1, Hq=8, Hkv=8, N=8192, d=256,
                                          dtype="bf16", causal=True, mult=3.0),
+    # Few heads, long context: too few query tiles to fill the GPU without split-KV.
+    "bf16_h2_n16384_d128_causal": dict(seed=1007, B=1, Hq=2, Hkv=2, N=16384, d=128,
+                                       dtype="bf16", causal=True),
 }
 
 

@@ -116,6 +116,26 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
                  const fa355_tuning *tuning, fa355_plan *plan);
 
 /*
+ * Split-KV forward: as fa_fwd (output in the input dtype), with each query tile's
+ * key/value range cut into num_splits contiguous pieces handled by separate
+ * workgroups, for shapes with too few query tiles to fill the GPU.  Partial
+ * results are combined exactly by the online-softmax merge rule ("MCU 上
+ * Transformer 模型的 Flash Attention 实现…", §二, merge equations):
+ * lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.
+ *   dtype      F16 or BF16; d in {64, 128}
+ *   num_splits 1 .. 16
+ *   o_part     device pointer, caller-owned fp32 workspace [num_splits,B,Hq,N,d]
+ *   lse_part   device pointer, caller-owned fp32 workspace [num_splits,B,Hq,N]
+ * Enqueues two kernels (partials, merge) on `stream`; allocates nothing.  The
+ * workspaces must be 16- and 4-byte aligned and overlap nothing else
+ * (FA355_ERR_ARG); num_splits out of range is FA355_ERR_ARG.
+ */
+int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                 fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
+                 hipStream_t stream);
+
+/*
  * Backward pass: the gradients of sum(O * dout) for O = fa_fwd(q, k, v), i.e. of
  * any loss L with dL/dO = dout ("FlashAttention (VI)", equation Attention,
  * differentiated; the forward pass keeps no N x N matrix for it, as the Ascend

@@ -161,6 +161,9 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
         c = 1.17549435e-38f;
     a.c = c;
     a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    a.num_splits = 1;
+    a.o_part = nullptr;
+    a.lse_part = nullptr;
 
     out.var = var;
     out.plan.br = br;
@@ -186,6 +189,69 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse,
                      in_dt, (int)c.var->out_f32, d, causal != 0, c.plan.br, c.plan.bc,
                      c.plan.grid, c.plan.lds_bytes);
     return c.var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
+struct SplitVariant {
+    int dtype;
+    int d;
+    int bc;
+    bool causal;
+    LaunchFn fn;
+};
+
+#define FA355_SPLIT_ROW(T, D, BC, W, C) {FA355_DT_##T, D, BC, C, &fa355::launch_fwd_split<fa355::T, D, BC, W, C>},
+const SplitVariant kSplitVariants[] = {
+    FA355_SPLIT_VARIANTS(FA355_SPLIT_ROW, BF16, 64)
+    FA355_SPLIT_VARIANTS(FA355_SPLIT_ROW, BF16, 128)
+    FA355_SPLIT_VARIANTS(FA355_SPLIT_ROW, F16, 64)
+    FA355_SPLIT_VARIANTS(FA355_SPLIT_ROW, F16, 128)
+};
+constexpr int kMaxSplits = 16;
+
+int run_split(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+              int Hkv, int N, int d, int causal, float scale, int dt, int num_splits,
+              float *o_part, float *lse_part, hipStream_t stream)
+{
+    if (!o_part || !lse_part)
+        return FA355_ERR_NULL;
+    if (dt != FA355_F16 && dt != FA355_BF16)
+        return FA355_ERR_UNSUPPORTED;
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return FA355_ERR_ARG;
+    // The split kernels use 128-row query tiles: 64-key blocks at d = 64, 32-key
+    // blocks at d = 128.
+    const fa355_tuning tile = {128, d == 64 ? 64 : 32};
+    Checked c;
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dt, dt,
+                      (d == 64 || d == 128) ? &tile : nullptr, c);
+    if (rc != FA355_OK)
+        return rc;
+    if (d != 64 && d != 128)
+        return FA355_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(o_part) % 16 || reinterpret_cast<uintptr_t>(lse_part) % 4)
+        return FA355_ERR_ALIGN;
+    const size_t rows = (size_t)B * Hq * N;
+    const size_t bp = (size_t)num_splits * rows * d * 4, bl = (size_t)num_splits * rows * 4;
+    const size_t nq = rows * d * 2, nkv = (size_t)B * Hkv * N * d * 2;
+    struct Span { const void *p; size_t n; };
+    const Span others[] = {{q, nq}, {k, nkv}, {v, nkv}, {o, nq}, {lse, lse ? rows * 4 : 0}};
+    for (const Span &x : others)
+        if (overlaps(o_part, bp, x.p, x.n) || overlaps(lse_part, bl, x.p, x.n))
+            return FA355_ERR_ARG;
+    if (overlaps(o_part, bp, lse_part, bl))
+        return FA355_ERR_ARG;
+    if ((int64_t)c.plan.grid * num_splits > INT_MAX)
+        return FA355_ERR_SHAPE;
+    const SplitVariant *var = nullptr;
+    for (const SplitVariant &x : kSplitVariants)
+        if (x.dtype == dt && x.d == d && x.bc == tile.bc && x.causal == (causal != 0))
+            var = &x;
+    if (!var)
+        return FA355_ERR_UNSUPPORTED;
+    c.args.num_splits = num_splits;
+    c.args.o_part = o_part;
+    c.args.lse_part = lse_part;
+    return var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
 }
 
 using BwdLaunchFn = hipError_t (*)(const fa355::BwdArgs &, hipStream_t);
@@ -333,6 +399,15 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
                    dtype, stream);
 }
 
-int fa_version(void) { return 110; }
+int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                 fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
+                 hipStream_t stream)
+{
+    return run_split(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, num_splits,
+                     o_part, lse_part, stream);
+}
+
+int fa_version(void) { return 120; }
 
 }  // extern "C"

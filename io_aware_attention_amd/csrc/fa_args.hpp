@@ -31,6 +31,12 @@ struct FwdArgs {
     int total_tiles;   // B * Hq * n_qtiles = grid size
     float c;           // |scale| * log2(e); FLT_MIN stands in for a zero scale
     uint32_t q_sign;   // 0x80008000 flips the sign of every 16-bit Q element
+    // Split-KV launches only: each query tile's key/value blocks are cut into
+    // num_splits contiguous ranges, one workgroup each; partial results land in
+    // o_part [num_splits,B,Hq,N,D] and lse_part [num_splits,B,Hq,N] (fp32).
+    int num_splits;
+    float *o_part;
+    float *lse_part;
 };
 
 // Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
@@ -58,6 +64,10 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+
+// Split-KV forward: the partial-result kernel, then the merge kernel.
+template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream);
 
 // The three backward kernels (delta, dK/dV, dQ), in order on `stream`.
 template <typename T, int D, bool CAUSAL>
@@ -87,3 +97,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
 // Backward variants: Z(T, D, CAUSAL), 16-bit inputs, head dims 64 and 128.
 #define FA355_BWD_VARIANTS(Z, T) Z(T, 64, false) Z(T, 64, true) Z(T, 128, false) Z(T, 128, true)
+
+// Split-KV variants: S(T, D, BC, WAVES, CAUSAL).
+#define FA355_SPLIT_VARIANTS(S, T, D)                                                 \
+    S(T, D, (D == 64 ? 64 : 32), 4, false) S(T, D, (D == 64 ? 64 : 32), 4, true)

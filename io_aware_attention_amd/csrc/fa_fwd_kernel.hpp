@@ -197,7 +197,10 @@ struct FwdTraits {
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
 };
 
-template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32>
+// SPLIT: the workgroup handles one of a.num_splits contiguous ranges of the tile's
+// key/value blocks and writes its partial result, normalised by its own row sum,
+// with its own lse, to a.o_part / a.lse_part; fa_fwd_merge_kernel combines them.
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC)))
 fa_fwd_kernel(FwdArgs a)
@@ -212,8 +215,14 @@ fa_fwd_kernel(FwdArgs a)
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
 
-    int bh, qt;
-    tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, a.B * a.Hq, CAUSAL, bh, qt);
+    int bh, qt, split = 0;
+    if constexpr (SPLIT) {
+        const int w = blockIdx.x / a.num_splits;
+        split = blockIdx.x - w * a.num_splits;
+        tile_of(w, a.total_tiles, a.n_qtiles, a.B * a.Hq, CAUSAL, bh, qt);
+    } else {
+        tile_of(blockIdx.x, a.total_tiles, a.n_qtiles, a.B * a.Hq, CAUSAL, bh, qt);
+    }
     const int b = bh / a.Hq;
     const int hk = (bh - b * a.Hq) / a.group;
     const int N = a.N;
@@ -239,7 +248,13 @@ fa_fwd_kernel(FwdArgs a)
     }
 
     const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
-    const int n_kv = (kv_len + BC - 1) / BC;
+    int t_begin = 0, n_kv = (kv_len + BC - 1) / BC;
+    if constexpr (SPLIT) {
+        // Split s takes blocks [s * chunk, (s + 1) * chunk) of the tile's range.
+        const int chunk = (n_kv + a.num_splits - 1) / a.num_splits;
+        t_begin = min(n_kv, split * chunk);
+        n_kv = min(n_kv, t_begin + chunk);
+    }
 
     // Per-lane source offsets of this wavefront's DMA instructions (loop-invariant):
     // instruction i = p * WAVES + wave fills slots 64 i .. 64 i + 63 of the stage.
@@ -287,20 +302,21 @@ fa_fwd_kernel(FwdArgs a)
     float le_part = 0.0f;      // fp32 sum of unrounded P, for lse (bf16 only)
     const float c = a.c;
 
-    dma_block(0, 0);
+    if (t_begin < n_kv)
+        dma_block(t_begin, 0);
     __syncthreads();
 
-    for (int t = 0; t < n_kv; ++t) {
+    for (int t = t_begin; t < n_kv; ++t) {
         const int j0 = t * BC;
         if (t + 1 < n_kv)
-            dma_block(t + 1, (t + 1) & 1);
+            dma_block(t + 1, (t + 1 - t_begin) & 1);
 
         // Blocks wholly above this wavefront's causal diagonal, and wavefronts
         // wholly past N, have nothing to add.
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {
-            const char *kb = smem + (t & 1) * Tr::STAGE + k_rd;
-            const char *vb = smem + (t & 1) * Tr::STAGE + v_rd;
+            const char *kb = smem + ((t - t_begin) & 1) * Tr::STAGE + k_rd;
+            const char *vb = smem + ((t - t_begin) & 1) * Tr::STAGE + v_rd;
 
             f32x16_t sacc[Tr::JB];
 #pragma unroll
@@ -359,13 +375,16 @@ fa_fwd_kernel(FwdArgs a)
                 m_run = m_new;
             }
 
+            // A split's first blocks can hide every key from some rows (m = -inf):
+            // subtract 0 there, so their weights are exp2(-inf) = 0, not NaN.
+            const float m_sub = (SPLIT && m_run == -__builtin_inff()) ? 0.0f : m_run;
             u32x4_t pf[Tr::KS];
 #pragma unroll
             for (int jb = 0; jb < Tr::JB; ++jb) {
                 float p[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_run));
+                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_sub));
                     if constexpr (M::kSeparateLseSum)
                         le_part += p[r];
                 }
@@ -406,7 +425,22 @@ fa_fwd_kernel(FwdArgs a)
         const f32x2_t ep = row_pair(le_part);
         le_tot = ep[0] + ep[1];
     }
-    if (iq < N) {
+    if (SPLIT && iq < N) {
+        // Rows that saw no key in this split: weight zero in the merge.
+        const bool none = l_tot == 0.0f;
+        const float inv = none ? 0.0f : 1.0f / l_tot;
+        const size_t prow = (size_t)split * a.B * a.Hq * N + (size_t)bh * N + iq;
+#pragma unroll
+        for (int nb = 0; nb < Tr::NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4_t y = {oacc[nb][4 * g] * inv, oacc[nb][4 * g + 1] * inv,
+                                   oacc[nb][4 * g + 2] * inv, oacc[nb][4 * g + 3] * inv};
+                *reinterpret_cast<f32x4_t *>(a.o_part + prow * D + nb * 32 + 8 * g + 4 * h2) = y;
+            }
+        if (h2 == 0)
+            a.lse_part[prow] = none ? -__builtin_inff() : kLn2 * (m_run + __log2f(le_tot));
+    } else if (iq < N) {
         const float inv = 1.0f / l_tot;
         const size_t orow = ((size_t)bh * N + iq) * D;
 #pragma unroll
@@ -427,6 +461,44 @@ fa_fwd_kernel(FwdArgs a)
         if (h2 == 0 && a.lse)
             a.lse[(size_t)bh * N + iq] = kLn2 * (m_run + __log2f(le_tot));
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge: the partial results of one query row over disjoint key ranges
+// combine exactly by the same rule as the online-softmax update ("MCU 上
+// Transformer 模型的 Flash Attention 实现…", §二, merge equations), applied to
+// normalised partials:  lse = log sum_s e^{lse_s},  O = sum_s e^{lse_s - lse} O_s.
+// D/4 threads per row, four columns each.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) fa_fwd_merge_kernel(FwdArgs a)
+{
+    constexpr int TPR = D / 4;
+    constexpr int RPB = 256 / TPR;
+    const int64_t rows = (int64_t)a.B * a.Hq * a.N;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int col = (threadIdx.x % TPR) * 4;
+    if (row >= rows)
+        return;
+    float m = -__builtin_inff();
+    for (int s = 0; s < a.num_splits; ++s)
+        m = fmaxf(m, a.lse_part[s * rows + row]);
+    float wsum = 0.0f;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < a.num_splits; ++s) {
+        const float ls = a.lse_part[s * rows + row];
+        if (ls == -__builtin_inff())
+            continue;
+        const float w = __builtin_amdgcn_exp2f((ls - m) * 1.44269504088896341f);
+        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(a.o_part + (s * rows + row) * D + col);
+        acc += w * x;
+        wsum += w;
+    }
+    const float inv = 1.0f / wsum;
+    const u32x2_t y = {Mfma<T>::pack(acc[0] * inv, acc[1] * inv), Mfma<T>::pack(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.o) + row * D + col) = y;
+    if (col == 0 && a.lse)
+        a.lse[row] = m + kLn2 * __log2f(wsum);
 }
 
 // ---------------------------------------------------------------------------

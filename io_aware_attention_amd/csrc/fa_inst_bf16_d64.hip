@@ -2,3 +2,4 @@
 #include "fa_launch.hpp"
 
 FA355_VARIANTS_D64_D128(FA355_INSTANTIATE, BF16, 64)
+FA355_SPLIT_VARIANTS(FA355_INSTANTIATE_SPLIT, BF16, 64)

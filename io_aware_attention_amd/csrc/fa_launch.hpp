@@ -19,6 +19,27 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
     return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, Tr::LDS, stream);
 }
 
+template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream)
+{
+    using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, false>;
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, false, true>);
+    static const hipError_t attr =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS);
+    if (attr != hipSuccess)
+        return attr;
+    FwdArgs arg = a;
+    void *params[] = {&arg};
+    hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles * a.num_splits), dim3(Tr::NT), params,
+                                   Tr::LDS, stream);
+    if (e != hipSuccess)
+        return e;
+    const int64_t rows = (int64_t)a.B * a.Hq * a.N;
+    constexpr int RPB = 256 / (D / 4);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_fwd_merge_kernel<T, D>),
+                           dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), params, 0, stream);
+}
+
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
 {
@@ -35,3 +56,5 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
     template hipError_t fa355::launch_fwd<fa355::T, D, BC, W, C, O>(const fa355::FwdArgs &, hipStream_t);
 #define FA355_INSTANTIATE_F32(W, C)                                                   \
     template hipError_t fa355::launch_fwd_f32<W, C>(const fa355::FwdArgs &, hipStream_t);
+#define FA355_INSTANTIATE_SPLIT(T, D, BC, W, C)                                       \
+    template hipError_t fa355::launch_fwd_split<fa355::T, D, BC, W, C>(const fa355::FwdArgs &, hipStream_t);

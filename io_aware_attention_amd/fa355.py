@@ -20,7 +20,8 @@ F32, F16, BF16 = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 
 # Every exported symbol, as declared in include/fa355.h.
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_bwd", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_bwd", "fa_status_str",
+           "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_ex.restype = ip
     L.fa_fwd_check.argtypes = common + [ip, ip, ctypes.POINTER(Tuning), ctypes.POINTER(Plan)]
     L.fa_fwd_check.restype = ip
+    L.fa_fwd_split.argtypes = common + [ip, ip, vp, vp, vp]
+    L.fa_fwd_split.restype = ip
     L.fa_bwd.argtypes = [vp] * 10 + [ip, ip, ip, ip, ip, ip, fp, ip, vp]
     L.fa_bwd.restype = ip
     L.fa_status_str.argtypes = [ip]
@@ -196,3 +199,44 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
                   ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return dq, dk, dv
+
+
+def split_count(B: int, Hq: int, N: int, causal: bool, cus: int = 256) -> int:
+    """A split count that gives the launch about four workgroups per compute unit,
+    keeping at least four key blocks per split (1 = no split)."""
+    tiles = B * Hq * ((N + 127) // 128)
+    want = -(-4 * cus // tiles)
+    blocks = (N + 31) // 32
+    return max(1, min(16, want, blocks // 4))
+
+
+def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, num_splits=None, *,
+              o=None, lse=None, o_part=None, lse_part=None, stream=None):
+    """Split-KV attention forward (16-bit inputs, d = 64 or 128): returns (o, lse).
+
+    num_splits defaults to split_count(); the fp32 workspaces o_part
+    [S,B,Hq,N,d] and lse_part [S,B,Hq,N] are allocated with torch unless given.
+    """
+    import torch
+    L = lib()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if num_splits is None:
+        num_splits = split_count(B, Hq, N, causal)
+    S = int(num_splits)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, N), **f32) if lse is None else lse
+    o_part = torch.empty((S, B, Hq, N, d), **f32) if o_part is None else o_part
+    lse_part = torch.empty((S, B, Hq, N), **f32) if lse_part is None else lse_part
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _dtype_code(q.dtype),
+                        S, o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse

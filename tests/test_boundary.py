@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = F.lib()
-    assert L.fa_version() == 110
+    assert L.fa_version() == 120
     for s in range(-6, 1):
         assert F.status_str(s) and F.status_str(s) != "unknown status"
     assert F.status_str(-99) == "unknown status"
