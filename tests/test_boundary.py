@@ -125,3 +125,20 @@ def bwd_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, do=BAS
 ])
 def test_bwd_rejections(kw, code):
     assert bwd_call(**kw) == code, kw
+
+
+def split_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+               B_=1, Hq=4, Hkv=2, N=100, d=128, causal=1, scale=0.1, dt=F.BF16, S=4,
+               op=BASE + 5 * SPAN, lp=BASE + 6 * SPAN):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_fwd_split(q, k, v, o, lse, B_, Hq, Hkv, N, d, causal, scale, dt, S, op, lp,
+                                None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), -1), (dict(lp=None), -1), (dict(q=None), -1), (dict(S=0), -5), (dict(S=17), -5),
+    (dict(d=256), -3), (dict(dt=F.F32, d=64), -3), (dict(N=0), -2), (dict(op=BASE + 5 * SPAN + 8), -4),
+    (dict(lp=BASE + 6 * SPAN + 2), -4), (dict(op=BASE + 8192), -5), (dict(lp=BASE + 5 * SPAN + 64), -5),
+])
+def test_split_rejections(kw, code):
+    assert split_call(**kw) == code, kw
