@@ -55,6 +55,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blocked_attention_fwd.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                           ip, ctypes.c_double, i64, i64]
     lib.blocked_attention_fwd.restype = ip
+    lib.oracle_attention_fwd_bias.argtypes = [dp, dp, dp, dp, i64, i64, i64, dp, dp, i64, i64,
+                                              i64, i64, i64, ip, ctypes.c_double, ip]
+    lib.oracle_attention_fwd_bias.restype = ip
     lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                          ip, ctypes.c_double, ip]
     lib.oracle_attention_bwd.restype = ip
@@ -107,6 +110,32 @@ def attention(q, k, v, causal: bool, scale: float, rows=None, threads: int = 0,
                                 _ptr(r), R, int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attention_fwd failed with {rc}")
+    return o, lse
+
+
+def attention_bias(q, k, v, bias, causal: bool, scale: float, threads: int = 0, lib=None):
+    """Exact attention with an additive bias on the scaled scores.
+
+    bias broadcasts to [B,Hq,N,N] (leading dimensions of size 1 are shared).
+    Rows whose every score is -inf give o = 0 and lse = -inf.  Returns (o, lse).
+    """
+    L = _get(lib)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    bias = np.asarray(bias, dtype=np.float64)
+    if bias.ndim != 4 or bias.shape[2:] != (N, N) or bias.shape[0] not in (1, B) \
+            or bias.shape[1] not in (1, Hq):
+        raise ValueError(f"bias shape {bias.shape} does not broadcast to {(B, Hq, N, N)}")
+    bias = np.ascontiguousarray(bias)
+    sb = 0 if bias.shape[0] == 1 else bias.shape[1] * N * N
+    sh = 0 if bias.shape[1] == 1 else N * N
+    o = np.empty((B, Hq, N, d), np.float64)
+    lse = np.empty((B, Hq, N), np.float64)
+    rc = L.oracle_attention_fwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), sb, sh, N,
+                                     _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+                                     float(scale), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_fwd_bias failed with {rc}")
     return o, lse
 
 

@@ -26,6 +26,11 @@
  *     GQA性能调优技术解析", GQA mechanism);
  *   - lse[b,h,i] = m_i + ln(l_i), natural log, in units of scaled scores.
  *
+ * With an additive bias (a fused-operator variant: "深度探索Flash-Attention中GQA性能
+ * 调优技术解析" and the FlashAttention-3 feature list of "FlashAttention (VI)"), the
+ * scores are s_ij = scale * q_i.k_j + bias[b,h,i,j]; a bias of -inf masks the pair.
+ * A row whose every score is -inf attends to nothing: o = 0, lse = -inf.
+ *
  * Layouts: q, o are [B,Hq,N,d]; k, v are [B,Hkv,N,d]; lse is [B,Hq,N]; all fp64,
  * contiguous, d innermost.  With a row list, o and lse hold only those rows, in
  * list order: o is [B,Hq,nrows,d], lse is [B,Hq,nrows].
@@ -43,6 +48,8 @@ typedef struct {
     int64_t B, Hq, Hkv, N, d;
     int causal;
     double scale;
+    const double *bias;    /* optional additive bias, element (b,h,i,j) at       */
+    int64_t sb, sh, si;    /* b*sb + h*sh + i*si + j (strides may be 0)         */
     const int64_t *rows;   /* query rows computed for every (b, h); NULL = all   */
     int64_t nrows;         /* length of the row list (N when rows == NULL)       */
     int64_t chunk;         /* rows per work unit                                 */
@@ -79,13 +86,16 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
         double *s = S + (r - r0) * N;
         const double *qi = qh + i * d;
 
-        /* Scores s_ij = scale * sum_t q_it k_jt, the full row materialised. */
+        /* Scores s_ij = scale * sum_t q_it k_jt (+ bias), the full row materialised. */
+        const double *brow = J->bias ? J->bias + b * J->sb + h * J->sh + i * J->si : NULL;
         for (int64_t j = 0; j < jend; ++j) {
             const double *kj = kh + j * d;
             double acc = 0.0;
             for (int64_t t = 0; t < d; ++t)
                 acc += qi[t] * kj[t];
             s[j] = J->scale * acc;
+            if (brow)
+                s[j] += brow[j];
         }
 
         /* Pass 1: the row maximum over the visible keys. */
@@ -94,14 +104,15 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
             if (s[j] > m)
                 m = s[j];
 
-        /* Pass 2: e_ij = exp(s_ij - m_i), l_i = sum_j e_ij; then P_ij = e_ij / l_i. */
+        /* Pass 2: e_ij = exp(s_ij - m_i), l_i = sum_j e_ij; then P_ij = e_ij / l_i.
+         * A row with no finite score (only possible with a bias) has P = 0. */
         double l = 0.0;
         for (int64_t j = 0; j < jend; ++j) {
-            s[j] = exp(s[j] - m);
+            s[j] = m == -INFINITY ? 0.0 : exp(s[j] - m);
             l += s[j];
         }
         for (int64_t j = 0; j < jend; ++j)
-            s[j] = s[j] / l;
+            s[j] = l > 0.0 ? s[j] / l : 0.0;
 
         /* O_i = sum_j P_ij v_j. */
         double *oi = J->o ? J->o + (bh * J->nrows + r) * d : NULL;
@@ -115,7 +126,7 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
             }
         }
         if (J->lse)
-            J->lse[bh * J->nrows + r] = m + log(l);
+            J->lse[bh * J->nrows + r] = l > 0.0 ? m + log(l) : -INFINITY;
         if (J->probs) {
             double *pr = J->probs + (bh * J->nrows + r) * N;
             for (int64_t j = 0; j < N; ++j)
@@ -257,4 +268,31 @@ int oracle_attention_probs(const double *q, const double *k, double *probs,
     J.rows = NULL;
     J.nrows = N;
     return run_job(&J, 1);
+}
+
+/*
+ * As oracle_attention_fwd, with an additive bias on the scaled scores: element
+ * (b, h, i, j) of the fp64 array `bias` sits at b*sb + h*sh + i*si + j.
+ */
+int oracle_attention_fwd_bias(const double *q, const double *k, const double *v,
+                              const double *bias, int64_t sb, int64_t sh, int64_t si,
+                              double *o, double *lse,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                              int causal, double scale, int threads)
+{
+    if (!q || !k || !v || !bias)
+        return -1;
+    int rc = check_args(B, Hq, Hkv, N, d, NULL, N);
+    if (rc)
+        return rc;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.probs = NULL;
+    J.bias = bias; J.sb = sb; J.sh = sh; J.si = si;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.causal = causal != 0;
+    J.scale = scale;
+    J.rows = NULL;
+    J.nrows = N;
+    return run_job(&J, threads);
 }

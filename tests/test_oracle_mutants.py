@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle_pins as P
 import grad_pins as GP
+import bias_pins as BP
 
 ORACLE = "attention_oracle.c"
 BLOCKED = "blocked_reference.c"
@@ -22,15 +23,15 @@ MUTANTS = [
     ("causal_strict", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i : N")]),
     ("causal_leak", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i + 2 : N")]),
     ("gqa_modulo", ORACLE, [("const int64_t hk = h / group;", "const int64_t hk = h % J->Hkv;")]),
-    ("exp_sign", ORACLE, [("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);")]),
+    ("exp_sign", ORACLE, [("exp(s[j] - m);", "exp(m - s[j]);")]),
     ("no_scale", ORACLE, [("s[j] = J->scale * acc;", "s[j] = acc;")]),
-    ("no_normalise", ORACLE, [("s[j] = s[j] / l;", "s[j] = s[j];")]),
+    ("no_normalise", ORACLE, [("s[j] = l > 0.0 ? s[j] / l : 0.0;", "s[j] = s[j];")]),
     ("drop_first_value", ORACLE, [("for (int64_t j = 0; j < jend; ++j) {\n                const double *vj",
                                    "for (int64_t j = 1; j < jend; ++j) {\n                const double *vj")]),
     ("value_row_i", ORACLE, [("const double *vj = vh + j * d;", "const double *vj = vh + i * d;")]),
     ("transposed_scores", ORACLE, [("const double *qi = qh + i * d;", "const double *qi = kh + i * d;"),
                                    ("const double *kj = kh + j * d;", "const double *kj = qh + j * d;")]),
-    ("lse_without_max", ORACLE, [("= m + log(l);", "= log(l);")]),
+    ("lse_without_max", ORACLE, [("? m + log(l) :", "? log(l) :")]),
     ("dot_skips_last", ORACLE, [("for (int64_t t = 0; t < d; ++t)\n                acc += qi[t] * kj[t];",
                                  "for (int64_t t = 0; t + 1 < d; ++t)\n                acc += qi[t] * kj[t];")]),
     ("key_head_not_query_head", ORACLE, [("const double *kh = J->k + (b * J->Hkv + hk) * N * d;",
@@ -43,6 +44,11 @@ MUTANTS = [
     ("blocked_local_max_ignored", BLOCKED, [("const double p = exp(sblk[j - j0] - mt);",
                                              "const double p = exp(sblk[j - j0] - mn_unused);"),
                                             ("double lt = 0.0;", "double lt = 0.0; const double mn_unused = (m[i] > mt) ? m[i] : mt;")]),
+    ("bias_ignored", ORACLE, [("s[j] += brow[j];", "s[j] += 0.0 * brow[j];")]),
+    ("bias_scaled", ORACLE, [("s[j] += brow[j];", "s[j] += J->scale * brow[j];")]),
+    ("bias_row_shift", ORACLE, [("+ i * J->si : NULL;", "+ (i > 0 ? i - 1 : 0) * J->si : NULL;")]),
+    ("bias_head_stride_ignored", ORACLE, [("h * J->sh", "0 * J->sh")]),
+    ("masked_row_lse_zero", ORACLE, [("l > 0.0 ? m + log(l) : -INFINITY", "l > 0.0 ? m + log(l) : 0.0")]),
     ("grad_no_row_term", GRAD, [("const double ds = p[j] * (dp[j] - pdp);", "const double ds = p[j] * dp[j];")]),
     ("grad_dk_unscaled", GRAD, [("dkh[j * d + t] += J->scale * ds * qi[t];", "dkh[j * d + t] += ds * qi[t];")]),
     ("grad_dq_from_v", GRAD, [("dqi[t] += J->scale * ds * kh[j * d + t];", "dqi[t] += J->scale * ds * vh[j * d + t];")]),
@@ -60,6 +66,7 @@ def _quick_oracle_pins(lib):
     P.pin_torch_sdpa(lib)
     P.pin_closed_forms(lib)
     P.pin_invariants(lib)
+    BP.all_bias_pins(lib)
 
 
 def _quick_grad_pins(lib):
