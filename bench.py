@@ -4,6 +4,7 @@
     python bench.py --profile-run      # a few launches + a calibration copy, for rocprofv3
     python bench.py --bwd [...]        # the backward pass (fa_bwd) on the same workload
     python bench.py --split [S] [...]  # the split-KV forward (fa_fwd_split)
+    python bench.py --bias KIND [...]  # the forward with an additive bias (fa_fwd_bias)
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
 batch of seeded synthetic inputs already resident in device memory.  The default
@@ -184,6 +185,15 @@ def run(args) -> dict:
             F.fwd_split(q, k, v, causal=x.causal, scale=x.scale, num_splits=S, o=o, lse=lse,
                         o_part=o_part, lse_part=lse_part, stream=stream)
 
+    if args.bias is not None:
+        shape = {"shared": (1, 1, x.N, x.N), "head": (1, x.Hq, x.N, x.N),
+                 "full": (x.B, x.Hq, x.N, x.N)}[args.bias]
+        bias = torch.from_numpy(G.make_normal(4243, shape, x.dtype))
+        bias = (bias.view(torch.bfloat16) if x.dtype == "bf16" else bias).to(dev)
+
+        def step():  # noqa: F811
+            F.fwd_bias(q, k, v, bias, causal=x.causal, scale=x.scale, o=o, lse=lse, stream=stream)
+
     if args.bwd:
         # The backward pass over the forward pass's own O and lse.
         step()
@@ -260,6 +270,10 @@ def run(args) -> dict:
                      "traffic": None if args.bwd else load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if args.bias is not None:
+        line["config"]["pass"] = f"forward with an additive bias (fa_fwd_bias, bias {list(shape)})"
+        line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
+        line["roofline"]["traffic"] = None
     if args.split is not None:
         line["config"]["pass"] = f"split-KV forward (fa_fwd_split, {S} splits: partials + merge)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
@@ -285,6 +299,9 @@ def main(argv=None) -> int:
     ap.add_argument("--split", type=int, nargs="?", const=0, default=None,
                     help="time the split-KV forward (fa_fwd_split) with this many splits "
                          "(no value: the binding's split_count)")
+    ap.add_argument("--bias", choices=("shared", "head", "full"), default=None,
+                    help="time fa_fwd_bias with an N(0,1) bias of shape [1,1,N,N], "
+                         "[1,Hq,N,N] or [B,Hq,N,N]")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) instead; FLOPs = 2.5x the forward's")
     args = ap.parse_args(argv)

@@ -244,13 +244,18 @@ def make_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str
                            int(seed), out[0], out[1], out[2], recipe, extra)
 
 
-def make_grad_output(seed: int, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
-    """A seeded upstream gradient dL/dO: N(0,1) draws (times mult), rounded, as storage."""
+def make_normal(seed: int, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
+    """Seeded N(0,1) draws (times mult) of `shape`, rounded to dtype, as storage."""
     st = Stream(seed)
     g = st.normals(int(np.prod(shape))).reshape(shape)
     if mult != 1.0:
         g *= mult
     return to_storage(round_to_dtype(g, dtype), dtype)
+
+
+def make_grad_output(seed: int, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
+    """A seeded upstream gradient dL/dO (see make_normal)."""
+    return make_normal(seed, shape, dtype, mult)
 
 
 # The six measured workloads.  Shapes follow the pages' layers: a 4096-token

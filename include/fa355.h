@@ -116,6 +116,30 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
                  const fa355_tuning *tuning, fa355_plan *plan);
 
 /*
+ * Forward with an additive bias on the scaled scores:
+ *     O = softmax(Q K^T * scale + bias) V
+ * (the fused additive bias / general mask of the FlashAttention feature lists:
+ * "深度探索Flash-Attention中GQA性能调优技术解析", and "FlashAttention (VI)" on
+ * FlashAttention-3).  A bias of -inf masks a (query, key) pair, so any mask can be
+ * given this way; a query row left with no finite score gets O = 0 and lse = -inf.
+ * Causal masking, if asked for, applies on top.
+ *   bias       device pointer, element type `dtype`; element (b, h, i, j) -- batch,
+ *              query head, query row, key -- at b*bias_stride_b + h*bias_stride_h +
+ *              i*bias_stride_row + j.  A stride of 0 shares the bias across that
+ *              dimension (e.g. one [N,N] bias for every batch and head).
+ *   strides    in elements; bias_stride_row >= N; all strides multiples of 4 and
+ *              bias 8-byte aligned (FA355_ERR_ALIGN); negative strides or a row
+ *              stride below N are FA355_ERR_ARG
+ *   dtype      F16 or BF16; d in {64, 128}; output in the input dtype
+ * Otherwise as fa_fwd.  Reads the bias once per (query row, key) it needs:
+ * B*Hq*N^2*2 bytes (halved when causal) on top of the forward's traffic.
+ */
+int fa_fwd_bias(const void *q, const void *k, const void *v, void *o, float *lse,
+                const void *bias, long long bias_stride_b, long long bias_stride_h,
+                long long bias_stride_row, int B, int Hq, int Hkv, int N, int d, int causal,
+                float scale, fa355_dtype dtype, hipStream_t stream);
+
+/*
  * Split-KV forward: as fa_fwd (output in the input dtype), with each query tile's
  * key/value range cut into num_splits contiguous pieces handled by separate
  * workgroups, for shapes with too few query tiles to fill the GPU.  Partial

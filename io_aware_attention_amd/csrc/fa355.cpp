@@ -164,6 +164,8 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
     a.num_splits = 1;
     a.o_part = nullptr;
     a.lse_part = nullptr;
+    a.bias = nullptr;
+    a.bias_sb = a.bias_sh = a.bias_si = 0;
 
     out.var = var;
     out.plan.br = br;
@@ -251,6 +253,59 @@ int run_split(const void *q, const void *k, const void *v, void *o, float *lse, 
     c.args.num_splits = num_splits;
     c.args.o_part = o_part;
     c.args.lse_part = lse_part;
+    return var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
+#define FA355_BIAS_ROW(T, D, BC, W, C) {FA355_DT_##T, D, BC, C, &fa355::launch_fwd_bias<fa355::T, D, BC, W, C>},
+const SplitVariant kBiasVariants[] = {
+    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, BF16, 64)
+    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, BF16, 128)
+    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, F16, 64)
+    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, F16, 128)
+};
+
+int run_bias(const void *q, const void *k, const void *v, void *o, float *lse,
+             const void *bias, long long sb, long long sh, long long si,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale, int dt,
+             hipStream_t stream)
+{
+    if (!bias)
+        return FA355_ERR_NULL;
+    if (dt != FA355_F16 && dt != FA355_BF16)
+        return FA355_ERR_UNSUPPORTED;
+    // The bias kernels use the split kernels' tiles: 128 rows, 64-key blocks at
+    // d = 64, 32-key blocks at d = 128.
+    const fa355_tuning tile = {128, d == 64 ? 64 : 32};
+    Checked c;
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dt, dt,
+                      (d == 64 || d == 128) ? &tile : nullptr, c);
+    if (rc != FA355_OK)
+        return rc;
+    if (d != 64 && d != 128)
+        return FA355_ERR_UNSUPPORTED;
+    // Rows are read four keys (8 bytes) at a time.
+    if (sb < 0 || sh < 0 || si < N)
+        return FA355_ERR_ARG;
+    if (reinterpret_cast<uintptr_t>(bias) % 8 || si % 4 || sh % 4 || sb % 4)
+        return FA355_ERR_ALIGN;
+    // One (batch, head) slice of the bias is addressed with 32-bit byte offsets.
+    if (((long long)(N - 1) * si + N) * 2 > INT_MAX - 65536)
+        return FA355_ERR_SHAPE;
+    const long long last = (long long)(B - 1) * sb + (long long)(Hq - 1) * sh + (long long)(N - 1) * si + N;
+    const size_t rows = (size_t)B * Hq * N;
+    if (overlaps(bias, (size_t)last * 2, o, rows * d * 2) ||
+        (lse && overlaps(bias, (size_t)last * 2, lse, rows * 4)))
+        return FA355_ERR_ARG;
+    const SplitVariant *var = nullptr;
+    for (const SplitVariant &x : kBiasVariants)
+        if (x.dtype == dt && x.d == d && x.bc == tile.bc && x.causal == (causal != 0))
+            var = &x;
+    if (!var)
+        return FA355_ERR_UNSUPPORTED;
+    c.args.bias = bias;
+    c.args.bias_sb = sb;
+    c.args.bias_sh = sh;
+    c.args.bias_si = si;
     return var->fn(c.args, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
 }
 
@@ -408,6 +463,15 @@ int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *ls
                      o_part, lse_part, stream);
 }
 
-int fa_version(void) { return 120; }
+int fa_fwd_bias(const void *q, const void *k, const void *v, void *o, float *lse,
+                const void *bias, long long bias_stride_b, long long bias_stride_h,
+                long long bias_stride_row, int B, int Hq, int Hkv, int N, int d, int causal,
+                float scale, fa355_dtype dtype, hipStream_t stream)
+{
+    return run_bias(q, k, v, o, lse, bias, bias_stride_b, bias_stride_h, bias_stride_row, B, Hq,
+                    Hkv, N, d, causal, scale, dtype, stream);
+}
+
+int fa_version(void) { return 130; }
 
 }  // extern "C"

@@ -37,6 +37,10 @@ struct FwdArgs {
     int num_splits;
     float *o_part;
     float *lse_part;
+    // Additive-bias launches only: element (b, h, i, j) of the 16-bit bias is at
+    // b * bias_sb + h * bias_sh + i * bias_si + j (strides in elements, 0 = shared).
+    const void *bias;
+    long long bias_sb, bias_sh, bias_si;
 };
 
 // Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
@@ -64,6 +68,10 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+
+// Forward with an additive bias on the scaled scores.
+template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+hipError_t launch_fwd_bias(const FwdArgs &a, hipStream_t stream);
 
 // Split-KV forward: the partial-result kernel, then the merge kernel.
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>

@@ -195,12 +195,16 @@ struct FwdTraits {
     // matrix work; head dim 256 needs the whole register file for one.
     static constexpr int OCC = (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+    static_assert(BR * (BC / 8) % (64 * WAVES) == 0, "bias tile DMA: whole instructions per wave");
 };
 
 // SPLIT: the workgroup handles one of a.num_splits contiguous ranges of the tile's
 // key/value blocks and writes its partial result, normalised by its own row sum,
 // with its own lse, to a.o_part / a.lse_part; fa_fwd_merge_kernel combines them.
-template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32, bool SPLIT = false>
+// BIAS: a 16-bit additive bias joins the scaled scores before the softmax (a bias
+// of -inf masks the pair; a row left with no finite score gets O = 0, lse = -inf).
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32, bool SPLIT = false,
+          bool BIAS = false>
 __global__ void __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC)))
 fa_fwd_kernel(FwdArgs a)
@@ -271,17 +275,47 @@ fa_fwd_kernel(FwdArgs a)
 
     // Block t of K and V into LDS stage `stage`.  The block's rows start each
     // buffer resource, so rows past N read as zero.
+    // With a bias, each stage also holds the bias tile of the block: BR rows of BC
+    // 16-bit values (BC * 2 bytes per row, rows contiguous), copied by the same DMA
+    // path as K and V, so each bias row is fetched as whole 16-byte chunks.
+    constexpr int B_CPR = BC / 8;                                   // chunks per row
+    constexpr int B_INSTR = BIAS ? Tr::BR * B_CPR / 64 : 0;
+    constexpr int STAGE = Tr::STAGE + (BIAS ? Tr::BR * BC * 2 : 0);
+    const char *bias_bh = nullptr;
+    int bias_bytes = 0;
+    if constexpr (BIAS) {
+        const int h = bh - b * a.Hq;
+        bias_bh = static_cast<const char *>(a.bias) + (b * a.bias_sb + h * a.bias_sh) * 2;
+        // The extent of the (b, h) slice, rounded up to whole dwords: buffer range
+        // checks zero any dword that is partly out of range, and the last valid key
+        // may share a dword with the element after it (same dword, same page).
+        bias_bytes = (int)((((long long)(N - 1) * a.bias_si + N) * 2 + 3) & ~3LL);
+    }
+
     auto dma_block = [&](int t, int stage) {
         const int j0 = t * BC;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)j0 * ROW, (N - j0) * ROW);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)j0 * ROW, (N - j0) * ROW);
-        char *st = smem + stage * Tr::STAGE;
+        char *st = smem + stage * STAGE;
 #pragma unroll
         for (int p = 0; p < Tr::P_INSTR; ++p) {
             const int i = p * WAVES + wave;
             if (Tr::N_INSTR % WAVES != 0 && i >= Tr::N_INSTR)
                 break;
             dma16(i < Tr::K_INSTR ? rk : rv, st + i * 1024, dma_off[p]);
+        }
+        if constexpr (BIAS) {
+            // Rows past N and keys past the (b, h) extent read as zero; keys past N
+            // inside it are masked later anyway.
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias_bh, bias_bytes);
+#pragma unroll
+            for (int p = 0; p < B_INSTR / WAVES; ++p) {
+                const int i = p * WAVES + wave;
+                const int slot = i * 64 + lane;
+                const int row = slot / B_CPR, ch = slot - row * B_CPR;
+                const int off = (int)((long long)(i0 + row) * a.bias_si * 2) + j0 * 2 + ch * 16;
+                dma16(rb, st + Tr::STAGE + i * 1024, i0 + row < N ? off : 0x7ffffff0);
+            }
         }
     };
 
@@ -300,7 +334,9 @@ fa_fwd_kernel(FwdArgs a)
     float m_run = -__builtin_inff();
     float l_part = 0.0f;       // this lane's half of the row sum of rounded P
     float le_part = 0.0f;      // fp32 sum of unrounded P, for lse (bf16 only)
-    const float c = a.c;
+    // With a bias the scores are taken to log2 units (x = s c + bias log2 e) as
+    // soon as they leave the matrix cores, and the multiplier below becomes 1.
+    const float c = BIAS ? 1.0f : a.c;
 
     if (t_begin < n_kv)
         dma_block(t_begin, 0);
@@ -315,8 +351,8 @@ fa_fwd_kernel(FwdArgs a)
         // wholly past N, have nothing to add.
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {
-            const char *kb = smem + ((t - t_begin) & 1) * Tr::STAGE + k_rd;
-            const char *vb = smem + ((t - t_begin) & 1) * Tr::STAGE + v_rd;
+            const char *kb = smem + ((t - t_begin) & 1) * STAGE + k_rd;
+            const char *vb = smem + ((t - t_begin) & 1) * STAGE + v_rd;
 
             f32x16_t sacc[Tr::JB];
 #pragma unroll
@@ -343,6 +379,33 @@ fa_fwd_kernel(FwdArgs a)
                         sacc[jb] = M::run(kf[kk][jb], qf[k0 + kk], sacc[jb]);
             }
 
+            if constexpr (BIAS) {
+                // Lane L's keys j0 + 32 jb + 8 g + 4 (L/32) + 0..3 of its row: four
+                // 16-bit values, one 8-byte LDS read.
+                const char *bb = smem + ((t - t_begin) & 1) * STAGE + Tr::STAGE +
+                                 (wave * 32 + l32) * BC * 2;
+#pragma unroll
+                for (int jb = 0; jb < Tr::JB; ++jb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(
+                            bb + (jb * 32 + 8 * g + 4 * h2) * 2);
+                        float bv[4];
+                        if constexpr (M::kSeparateLseSum) {        // bf16
+                            bv[0] = __uint_as_float(w[0] << 16); bv[1] = __uint_as_float(w[0] & 0xffff0000u);
+                            bv[2] = __uint_as_float(w[1] << 16); bv[3] = __uint_as_float(w[1] & 0xffff0000u);
+                        } else {                                    // f16, one half at a time
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                bv[e] = (float)__builtin_bit_cast(
+                                    _Float16, (uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sacc[jb][4 * g + e] = __builtin_fmaf(sacc[jb][4 * g + e], a.c,
+                                                                 bv[e] * 1.44269504088896341f);
+                    }
+            }
             if ((CAUSAL && j0 + BC - 1 > iw0) || j0 + BC > N) {
 #pragma unroll
                 for (int jb = 0; jb < Tr::JB; ++jb)
@@ -365,7 +428,10 @@ fa_fwd_kernel(FwdArgs a)
 
             if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
                 const float m_new = fmaxf(m_run, mt);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                // A row that has seen no finite score yet keeps m = -inf (possible
+                // with a bias or a key-range split): nothing to scale, alpha = 1.
+                const float alpha = ((SPLIT || BIAS) && m_new == -__builtin_inff())
+                                        ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_part *= alpha;
                 if constexpr (M::kSeparateLseSum)
                     le_part *= alpha;
@@ -377,7 +443,7 @@ fa_fwd_kernel(FwdArgs a)
 
             // A split's first blocks can hide every key from some rows (m = -inf):
             // subtract 0 there, so their weights are exp2(-inf) = 0, not NaN.
-            const float m_sub = (SPLIT && m_run == -__builtin_inff()) ? 0.0f : m_run;
+            const float m_sub = ((SPLIT || BIAS) && m_run == -__builtin_inff()) ? 0.0f : m_run;
             u32x4_t pf[Tr::KS];
 #pragma unroll
             for (int jb = 0; jb < Tr::JB; ++jb) {
@@ -441,7 +507,9 @@ fa_fwd_kernel(FwdArgs a)
         if (h2 == 0)
             a.lse_part[prow] = none ? -__builtin_inff() : kLn2 * (m_run + __log2f(le_tot));
     } else if (iq < N) {
-        const float inv = 1.0f / l_tot;
+        // With a bias a row can be left with no finite score: O = 0, lse = -inf.
+        const bool none = BIAS && l_tot == 0.0f;
+        const float inv = none ? 0.0f : 1.0f / l_tot;
         const size_t orow = ((size_t)bh * N + iq) * D;
 #pragma unroll
         for (int nb = 0; nb < Tr::NB; ++nb)
@@ -459,7 +527,7 @@ fa_fwd_kernel(FwdArgs a)
                 }
             }
         if (h2 == 0 && a.lse)
-            a.lse[(size_t)bh * N + iq] = kLn2 * (m_run + __log2f(le_tot));
+            a.lse[(size_t)bh * N + iq] = none ? -__builtin_inff() : kLn2 * (m_run + __log2f(le_tot));
     }
 }
 

@@ -20,6 +20,21 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 }
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+hipError_t launch_fwd_bias(const FwdArgs &a, hipStream_t stream)
+{
+    using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, false>;
+    constexpr int LDS = 2 * (Tr::STAGE + Tr::BR * BC * 2);      // K, V and bias tiles
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, false, false, true>);
+    static const hipError_t attr =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess)
+        return attr;
+    FwdArgs arg = a;
+    void *params[] = {&arg};
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, LDS, stream);
+}
+
+template <typename T, int D, int BC, int WAVES, bool CAUSAL>
 hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, false>;
@@ -58,3 +73,5 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
     template hipError_t fa355::launch_fwd_f32<W, C>(const fa355::FwdArgs &, hipStream_t);
 #define FA355_INSTANTIATE_SPLIT(T, D, BC, W, C)                                       \
     template hipError_t fa355::launch_fwd_split<fa355::T, D, BC, W, C>(const fa355::FwdArgs &, hipStream_t);
+#define FA355_INSTANTIATE_BIAS(T, D, BC, W, C)                                        \
+    template hipError_t fa355::launch_fwd_bias<fa355::T, D, BC, W, C>(const fa355::FwdArgs &, hipStream_t);

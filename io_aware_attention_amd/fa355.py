@@ -20,8 +20,8 @@ F32, F16, BF16 = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 
 # Every exported symbol, as declared in include/fa355.h.
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_bwd", "fa_status_str",
-           "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_fwd_bias", "fa_bwd",
+           "fa_status_str", "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_check.restype = ip
     L.fa_fwd_split.argtypes = common + [ip, ip, vp, vp, vp]
     L.fa_fwd_split.restype = ip
+    ll = ctypes.c_longlong
+    L.fa_fwd_bias.argtypes = [vp, vp, vp, vp, vp, vp, ll, ll, ll] + [ip] * 6 + [fp, ip, vp]
+    L.fa_fwd_bias.restype = ip
     L.fa_bwd.argtypes = [vp] * 10 + [ip, ip, ip, ip, ip, ip, fp, ip, vp]
     L.fa_bwd.restype = ip
     L.fa_status_str.argtypes = [ip]
@@ -238,5 +241,44 @@ def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, num_spl
     rc = L.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _dtype_code(q.dtype),
                         S, o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse
+
+
+def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, *, o=None,
+             lse=None, stream=None):
+    """Attention forward with an additive bias: softmax(Q K^T scale + bias) V.
+
+    bias: a tensor of q's dtype that broadcasts to [B,Hq,N,N] (size-1 leading
+    dimensions are shared); its last dimension must be contiguous.  A layout whose
+    strides are not multiples of 4 elements is first copied to a padded one.
+    Returns (o, lse).
+    """
+    import torch
+    L = lib()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if bias.dim() != 4 or tuple(bias.shape[2:]) != (N, N) or bias.shape[0] not in (1, B) \
+            or bias.shape[1] not in (1, Hq) or bias.dtype != q.dtype or bias.stride(3) != 1:
+        raise FA355Error(ERR_SHAPE, f"bias {tuple(bias.shape)} does not fit [B,Hq,N,N] of q's dtype")
+    if bias.stride(2) % 4 or (bias.shape[1] > 1 and bias.stride(1) % 4) or \
+            (bias.shape[0] > 1 and bias.stride(0) % 4) or bias.data_ptr() % 8:
+        # The kernel reads four keys per 8-byte load: give rows a stride that is a
+        # multiple of 4 elements (a padded copy).
+        Np = (N + 3) // 4 * 4
+        padded = torch.zeros(tuple(bias.shape[:3]) + (Np,), dtype=bias.dtype, device=bias.device)
+        padded[..., :N] = bias
+        bias = padded[..., :N]
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    sh = 0 if bias.shape[1] == 1 else bias.stride(1)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       bias.data_ptr(), sb, sh, bias.stride(2), B, Hq, Hkv, N, d,
+                       int(bool(causal)), float(scale), _dtype_code(q.dtype),
+                       ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return o, lse

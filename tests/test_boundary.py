@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = F.lib()
-    assert L.fa_version() == 120
+    assert L.fa_version() == 130
     for s in range(-6, 1):
         assert F.status_str(s) and F.status_str(s) != "unknown status"
     assert F.status_str(-99) == "unknown status"
@@ -142,3 +142,21 @@ def split_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=
 ])
 def test_split_rejections(kw, code):
     assert split_call(**kw) == code, kw
+
+
+def bias_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+              bias=BASE + 5 * SPAN, sb=0, sh=100 * 100, si=100, B_=1, Hq=4, Hkv=2, N=100, d=128,
+              causal=1, scale=0.1, dt=F.BF16):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_fwd_bias(q, k, v, o, lse, bias, sb, sh, si, B_, Hq, Hkv, N, d, causal, scale,
+                               dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bias=None), -1), (dict(q=None), -1), (dict(si=99), -5), (dict(sb=-4), -5),
+    (dict(bias=BASE + 5 * SPAN + 2), -4), (dict(si=102), -4), (dict(sh=10002), -4),
+    (dict(d=256), -3), (dict(dt=F.F32, d=64), -3), (dict(bias=BASE + 3 * SPAN + 64), -5),
+    (dict(N=1 << 16, si=1 << 16, sh=1 << 32), -2), (dict(Hq=3), -2),
+])
+def test_bias_rejections(kw, code):
+    assert bias_call(**kw) == code, kw
