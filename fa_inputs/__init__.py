@@ -20,6 +20,14 @@ Fill order
     follow V and beta_h = 2 u_h is added to every element of Q[:, h].  Values are
     multiplied (then biased) in fp64 and rounded once, fp64 -> storage dtype,
     round-to-nearest-even.
+
+8-bit inputs ("e4m3")
+    OCP e4m3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; normals
+    (1 + f/8) 2^(E-7) for E = 1..15, subnormals f 2^-9, largest finite 448 (code
+    0x7e), codes 0x7f / 0xff NaN.  Each tensor gets one descale, the fp32 value of
+    max|x| / 448 (1 for an all-zero tensor); the stored codes are x / descale,
+    clipped to [-448, 448] and rounded once to e4m3, and the value of an element is
+    descale * e4m3(code) (exact in fp64).
 """
 from __future__ import annotations
 
@@ -32,7 +40,7 @@ import numpy as np
 
 __all__ = [
     "splitmix64", "Stream", "round_to_dtype", "to_storage", "storage_to_f64",
-    "AttentionInputs", "make_inputs", "WORKLOADS", "workload",
+    "AttentionInputs", "make_inputs", "WORKLOADS", "workload", "quantize_e4m3",
 ]
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -102,6 +110,7 @@ class Stream:
 _FORMATS = {
     "bf16": (8, -126, float.fromhex("0x1.fep127")),
     "f16": (11, -14, 65504.0),
+    "e4m3": (4, -6, 448.0),
 }
 
 
@@ -173,7 +182,41 @@ def to_storage(x_rounded: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         bits = x_rounded.astype(np.float32).view(np.uint32) >> np.uint32(16)
         return bits.astype(np.uint16).view(np.int16)
+    if dtype == "e4m3":
+        return _e4m3_codes(x_rounded)
     raise ValueError(dtype)
+
+
+def _e4m3_codes(r: np.ndarray) -> np.ndarray:
+    """uint8 codes of values already on the e4m3 grid (finite, |r| <= 448)."""
+    r = np.asarray(r, dtype=np.float64)
+    a = np.abs(r)
+    if not (np.isfinite(a).all() and (a <= 448.0).all()):
+        raise ValueError("e4m3 values must be finite and at most 448 in magnitude")
+    m, e = np.frexp(a)                        # a = m 2^e, m in [0.5, 1)
+    normal = a >= 2.0 ** -6
+    E = np.where(normal, e.astype(np.int64) + 6, 0)
+    F = np.where(normal, (2.0 * m - 1.0) * 8.0, a * 2.0 ** 9)
+    if not np.array_equal(F, np.round(F)):
+        raise ValueError("value not on the e4m3 grid")
+    sign = np.signbit(r).astype(np.int64) << 7
+    return (sign | (E << 3) | F.astype(np.int64)).astype(np.uint8)
+
+
+def _e4m3_values(c: np.ndarray) -> np.ndarray:
+    c = np.asarray(c).view(np.uint8).astype(np.int64)
+    E, F = (c >> 3) & 15, c & 7
+    v = np.where(E == 0, F * 2.0 ** -9, (1.0 + F / 8.0) * np.exp2(E - 7.0))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return np.where(c & 0x80, -v, v)
+
+
+def quantize_e4m3(x: np.ndarray) -> tuple[np.ndarray, float]:
+    """Per-tensor e4m3 quantisation (module docstring): returns (codes, descale)."""
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    y = np.clip(x / descale, -448.0, 448.0)
+    return _e4m3_codes(round_to_dtype(y, "e4m3")), descale
 
 
 def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -181,6 +224,8 @@ def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         u32 = a.view(np.uint16).astype(np.uint32) << np.uint32(16)
         return u32.view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        return _e4m3_values(a)
     return a.astype(np.float64)
 
 
@@ -201,9 +246,13 @@ class AttentionInputs:
     v: np.ndarray
     recipe: str = ""
     extra: dict = field(default_factory=dict)
+    descale: tuple | None = None   # e4m3 inputs: (q, k, v) descales
 
     def f64(self, name: str) -> np.ndarray:
-        return storage_to_f64(getattr(self, name), self.dtype)
+        x = storage_to_f64(getattr(self, name), self.dtype)
+        if self.descale is not None:
+            x *= self.descale["qkv".index(name)]
+        return x
 
     @property
     def flops(self) -> float:
@@ -235,13 +284,21 @@ def make_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str
         beta = 2.0 * st.uniforms(Hq)
         q += beta[None, :, None, None]
         extra["q_head_bias"] = beta
-    out = []
-    for x in (q, k, v):
-        out.append(to_storage(round_to_dtype(x, dtype), dtype))
-        del x
+    out, descale = [], None
+    if dtype == "e4m3":
+        descale = []
+        for x in (q, k, v):
+            codes, ds = quantize_e4m3(x)
+            out.append(codes)
+            descale.append(ds)
+        descale = tuple(descale)
+    else:
+        for x in (q, k, v):
+            out.append(to_storage(round_to_dtype(x, dtype), dtype))
+            del x
     return AttentionInputs(B, Hq, Hkv, N, d, dtype, bool(causal),
                            default_scale(d) if scale is None else float(np.float32(scale)),
-                           int(seed), out[0], out[1], out[2], recipe, extra)
+                           int(seed), out[0], out[1], out[2], recipe, extra, descale)
 
 
 def make_normal(seed: int, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
@@ -278,6 +335,9 @@ WORKLOADS = {
     # Few heads, long context: too few query tiles to fill the GPU without split-KV.
     "bf16_h2_n16384_d128_causal": dict(seed=1007, B=1, Hq=2, Hkv=2, N=16384, d=128,
                                        dtype="bf16", causal=True),
+    # The 4096-token layer with e4m3 inputs and per-tensor descales.
+    "e4m3_h32_n4096_d128_causal": dict(seed=1008, B=1, Hq=32, Hkv=32, N=4096, d=128,
+                                       dtype="e4m3", causal=True),
 }
 
 

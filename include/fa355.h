@@ -185,6 +185,27 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            fa355_dtype dtype, hipStream_t stream);
 
+/*
+ * Forward with 8-bit floating-point inputs (the FP8 variant of "深度探索Flash-Attention
+ * 中GQA性能调优技术解析", FP8 section, and of FlashAttention-3 in "Flash Attention là
+ * gì"): q, k, v hold OCP e4m3 codes (1 sign bit, 4 exponent bits with bias 7, 3
+ * fraction bits; largest finite 448; 0x7f and 0xff are NaN), one byte per element,
+ * layouts as above.  Each tensor has one fp32 descale: the value of a stored code x
+ * is descale * e4m3(x).  Computes the forward pass on those values:
+ *     O = softmax((q_descale q)(k_descale k)^T * scale) (v_descale v)
+ *   o          device pointer [B,Hq,N,d] bf16; written
+ *   lse        device pointer [B,Hq,N] fp32 (natural log, scaled units), or NULL
+ *   q_descale, k_descale, v_descale   finite and > 0 (else FA355_ERR_ARG)
+ *   d          64 or 128
+ * The attention weights are rounded to e4m3 for the P V product (relative error up
+ * to 2^-4 per weight, before normalisation by the unrounded row sum); lse is taken
+ * from the unrounded weights.  Otherwise as fa_fwd: one kernel, nothing allocated,
+ * validation before any HIP call.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
 /* A static, human-readable name for a status code ("unknown status" otherwise). */
 const char *fa_status_str(int status);
 

@@ -1,6 +1,6 @@
 """MI355X-native FlashAttention forward and backward passes (libfa355) and their
 Python binding."""
 from .fa355 import (BF16, F16, F32, FA355Error, Plan, bwd, fwd, fwd_bias,  # noqa: F401
-                    fwd_split, lib, plan, split_count, status_str)
+                    fwd_fp8, fwd_split, lib, plan, split_count, status_str)
 
-__version__ = "0.2.0"
+__version__ = "0.3.0"

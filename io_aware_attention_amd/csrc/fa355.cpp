@@ -166,6 +166,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
     a.lse_part = nullptr;
     a.bias = nullptr;
     a.bias_sb = a.bias_sh = a.bias_si = 0;
+    a.o_scale = 1.0f;
 
     out.var = var;
     out.plan.br = br;
@@ -398,6 +399,76 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     return var->fn(a, stream) == hipSuccess ? FA355_OK : FA355_ERR_HIP;
 }
 
+// 8-bit (e4m3) inputs, bf16 output: 128-row query tiles, 64-key blocks.
+constexpr int kFp8Rows = 128;
+
+int run_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+            float q_descale, float k_descale, float v_descale, hipStream_t stream)
+{
+    if (!q || !k || !v || !o)
+        return FA355_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+    if (d != 64 && d != 128)
+        return FA355_ERR_UNSUPPORTED;
+    if ((int64_t)N * d * 2 > INT_MAX - 65536)       // one head of o, 32-bit offsets
+        return FA355_ERR_SHAPE;
+    const float ds[] = {q_descale, k_descale, v_descale};
+    for (float x : ds)
+        if (!std::isfinite(x) || !(x > 0.0f))
+            return FA355_ERR_ARG;
+    if (!std::isfinite(scale))
+        return FA355_ERR_ARG;
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
+        reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(o) % 16 ||
+        reinterpret_cast<uintptr_t>(lse) % 4)
+        return FA355_ERR_ALIGN;
+    const size_t nq = (size_t)B * Hq * N * d, nkv = (size_t)B * Hkv * N * d;
+    const size_t bo = nq * 2, bl = (size_t)B * Hq * N * sizeof(float);
+    if (overlaps(o, bo, q, nq) || overlaps(o, bo, k, nkv) || overlaps(o, bo, v, nkv))
+        return FA355_ERR_ARG;
+    if (lse && (overlaps(lse, bl, q, nq) || overlaps(lse, bl, k, nkv) ||
+                overlaps(lse, bl, v, nkv) || overlaps(lse, bl, o, bo)))
+        return FA355_ERR_ARG;
+    const int64_t n_qtiles = (N + kFp8Rows - 1) / kFp8Rows;
+    const int64_t tiles = (int64_t)B * Hq * n_qtiles;
+    if (tiles > INT_MAX)
+        return FA355_ERR_SHAPE;
+
+    fa355::FwdArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.group = Hq / Hkv;
+    a.n_qtiles = (int)n_qtiles;
+    a.total_tiles = (int)tiles;
+    // The Q and K descales join the score multiplier (computed in double, rounded
+    // once); a negative scale flips the sign bit of every Q byte (exact).
+    float c = (float)(std::fabs((double)scale) * (double)q_descale * (double)k_descale *
+                      1.4426950408889634);
+    if (!(c >= 1.17549435e-38f))
+        c = 1.17549435e-38f;
+    if (!std::isfinite(c))
+        return FA355_ERR_ARG;
+    a.c = c;
+    a.q_sign = scale < 0.0f ? 0x80808080u : 0u;
+    a.num_splits = 1;
+    a.o_scale = v_descale;
+    hipError_t e;
+    if (d == 64)
+        e = causal ? fa355::launch_fwd_fp8<64, true>(a, stream) : fa355::launch_fwd_fp8<64, false>(a, stream);
+    else
+        e = causal ? fa355::launch_fwd_fp8<128, true>(a, stream) : fa355::launch_fwd_fp8<128, false>(a, stream);
+    return e == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -472,6 +543,14 @@ int fa_fwd_bias(const void *q, const void *k, const void *v, void *o, float *lse
                     Hkv, N, d, causal, scale, dtype, stream);
 }
 
-int fa_version(void) { return 130; }
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               float q_descale, float k_descale, float v_descale, hipStream_t stream)
+{
+    return run_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, q_descale, k_descale,
+                   v_descale, stream);
+}
+
+int fa_version(void) { return 140; }
 
 }  // extern "C"

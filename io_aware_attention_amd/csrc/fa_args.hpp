@@ -41,6 +41,8 @@ struct FwdArgs {
     // b * bias_sb + h * bias_sh + i * bias_si + j (strides in elements, 0 = shared).
     const void *bias;
     long long bias_sb, bias_sh, bias_si;
+    // 8-bit-input launches only: the output multiplier (the V descale).
+    float o_scale;
 };
 
 // Backward pass: gradients of sum(O * dO) with respect to Q, K and V.
@@ -76,6 +78,10 @@ hipError_t launch_fwd_bias(const FwdArgs &a, hipStream_t stream);
 // Split-KV forward: the partial-result kernel, then the merge kernel.
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
 hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream);
+
+// Forward with e4m3 inputs (bf16 output), head dims 64 and 128.
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_fp8(const FwdArgs &a, hipStream_t stream);
 
 // The three backward kernels (delta, dK/dV, dQ), in order on `stream`.
 template <typename T, int D, bool CAUSAL>

@@ -21,7 +21,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -
 
 # Every exported symbol, as declared in include/fa355.h.
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_fwd_bias", "fa_bwd",
-           "fa_status_str", "fa_version")
+           "fa_fwd_fp8", "fa_status_str", "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_bias.restype = ip
     L.fa_bwd.argtypes = [vp] * 10 + [ip, ip, ip, ip, ip, ip, fp, ip, vp]
     L.fa_bwd.restype = ip
+    L.fa_fwd_fp8.argtypes = common + [fp, fp, fp, vp]
+    L.fa_fwd_fp8.restype = ip
     L.fa_status_str.argtypes = [ip]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -280,5 +282,40 @@ def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, *,
                        bias.data_ptr(), sb, sh, bias.stride(2), B, Hq, Hkv, N, d,
                        int(bool(causal)), float(scale), _dtype_code(q.dtype),
                        ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse
+
+
+def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+            causal: bool = False, scale: float | None = None, *, o=None, lse=None,
+            stream=None):
+    """Attention forward on e4m3 inputs: returns (o bf16, lse fp32).
+
+    q: [B,Hq,N,d]; k, v: [B,Hkv,N,d]; contiguous device tensors of e4m3 codes
+    (torch.uint8 or torch.float8_e4m3fn), d = 64 or 128.  The value of each element
+    is its tensor's descale times the code's e4m3 value.
+    """
+    import torch
+    L = lib()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in ok:
+            raise FA355Error(ERR_UNSUPPORTED, f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn)")
+        if not t.is_cuda or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device) if o is None else o
+    if tuple(o.shape) != (B, Hq, N, d) or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise FA355Error(ERR_ARG, "o has the wrong shape, dtype or layout")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, Hq, Hkv, N, d, int(bool(causal)), float(scale), float(q_descale),
+                      float(k_descale), float(v_descale), ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return o, lse

@@ -76,7 +76,10 @@ def oracle_heads(x: AttentionInputs, heads, rows=None, threads=0):
 def _slice64(x: AttentionInputs, name: str, b: int, h: int) -> np.ndarray:
     from fa_inputs import storage_to_f64
     a = getattr(x, name)[b:b + 1, h:h + 1]
-    return storage_to_f64(np.ascontiguousarray(a), x.dtype)
+    v = storage_to_f64(np.ascontiguousarray(a), x.dtype)
+    if x.descale is not None:
+        v *= x.descale["qkv".index(name)]
+    return v
 
 
 def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray,

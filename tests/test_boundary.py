@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = F.lib()
-    assert L.fa_version() == 130
+    assert L.fa_version() == 140
     for s in range(-6, 1):
         assert F.status_str(s) and F.status_str(s) != "unknown status"
     assert F.status_str(-99) == "unknown status"
@@ -160,3 +160,21 @@ def bias_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=B
 ])
 def test_bias_rejections(kw, code):
     assert bias_call(**kw) == code, kw
+
+
+def fp8_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+             B_=1, Hq=4, Hkv=2, N=100, d=128, causal=1, scale=0.1, dq=0.01, dk=0.01, dv=0.01):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_fwd_fp8(q, k, v, o, lse, B_, Hq, Hkv, N, d, causal, scale, dq, dk, dv, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(B_=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(N=0), -2), (dict(N=1 << 30), -2), (dict(d=256), -3),
+    (dict(d=96), -3), (dict(scale=float("inf")), -5), (dict(dq=0.0), -5), (dict(dk=-1.0), -5),
+    (dict(dv=float("nan")), -5), (dict(dq=float("inf")), -5), (dict(dq=1e30, dk=1e30), -5),
+    (dict(q=BASE + 8), -4), (dict(o=BASE + 3 * SPAN + 2), -4), (dict(lse=BASE + 4 * SPAN + 1), -4),
+    (dict(o=BASE + 32), -5), (dict(lse=BASE + 2 * SPAN + 16), -5), (dict(lse=BASE + 3 * SPAN + 64), -5),
+])
+def test_fp8_rejections(kw, code):
+    assert fp8_call(**kw) == code, kw

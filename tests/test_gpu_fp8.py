@@ -1,0 +1,198 @@
+"""GPU parity of the e4m3 forward pass (fa_fwd_fp8) against the fp64 oracle.
+
+The oracle takes the dequantised inputs (descale times the e4m3 value of each
+code, exact in fp64) through its plain definition of attention.  The kernel's
+rounding steps, with w_ij the oracle's softmax weights, w*_i = max_j w_ij and v
+the dequantised V:
+
+* scores: a product of two e4m3 values is exact, but the matrix instruction
+  (v_mfma_f32_32x32x64_f8f6f4) adds each group of 8 consecutive products with
+  every product but the group's largest truncated toward zero to a multiple of
+  2^(E-13), E the exponent of that largest product; the group sums and the
+  accumulator input are then added in fp32.  (Measured on MI355X with e4m3
+  operands: beside a product of 65536, products of 1..7 vanish, 10 and 14 become
+  8, -14 becomes -8, 8 and 16 stay; the same holds beside 98304, 114688 and
+  73728; a lone product of 1 added to an accumulator of 65536 is exact.)  With
+  the bytes of each lane's operand in head-dim order, the groups are 8 consecutive
+  dimensions, and the score error is at most
+      e_ij = |scale| dq dk T_ij,  T_ij = sum over groups G, t in G of (|q_it k_jt| mod g_G)
+  in raw e4m3 units (g_G = 2^(E_G - 13)), plus the fp32 terms: the multiplier
+  c = |scale| dq dk log2 e (two roundings), exp2 (about 2^-21) and the fp32 sum
+  across k steps, (d + 2) 2^-24 |q||k|^T;
+* P.V runs on the same instruction, groups of 8 keys: each group loses less than
+  7 steps of 2^-13 of its largest product, at most 2^-10 (1 + 2^-4) sum_j w_ij |v_jt|
+  in all, plus its fp32 accumulation over key blocks, (N/64 + 64) 2^-24 of that sum;
+* each weight exp2(x - m + 4), where m is at most the row maximum, is rounded to
+  e4m3: relative error <= 2^-4 (3 fraction bits) in the normal range; below it an
+  absolute error <= 2^-10 (half the subnormal step 2^-9), which the prescale 2^4
+  makes <= 2^-14 w*_i in units of the normalised weights;
+* the row sum L is the fp32 sum of the unrounded weights (relative error
+  <= N 2^-24 + max eps); dividing by it, the V descale and the bf16 store add
+  2^-22 relative and half a bf16 ulp.
+
+With eps_ij the sum of the relative weight errors above (score terms and P.V terms):
+    |err_it| <= sum_j (2^-4 w_ij + 2^-14 w*_i + eps_ij w_ij) |v_jt|
+                + (N 2^-24 + max_j eps_ij + 2^-22) |O_it| + ulp_bf16(O_it) / 2.
+The tests allow twice this (plus 1e-6 of the largest |O|).  A worst-case bound is
+loose for long rows, so the mean square error is also held to twice its expected
+value for independent round-to-nearest weight errors, plus the square of the
+(possibly biased) score and P.V terms:
+    E err_it^2 <= sum_j ((2^-3 w_ij)^2 / 12 + (2^-14 w*_i)^2) v_jt^2
+                  + (sum_j eps_ij w_ij |v_jt|)^2 + ulp_bf16(O_it)^2 / 12
+(a normal e4m3 step is at most 2^-3 of the value; a rounding error is uniform over
+one step).  lse: the 1e-3 of the 16-bit inputs plus twice the largest score error
+of the row, max_j e_ij (lse moves by at most the largest change of a score).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs as G
+import io_aware_attention_amd as F
+import oracle
+import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def run_fp8(x, scale=None, descale=None):
+    q, k, v = PT.to_device(x)
+    dq, dk, dv = x.descale if descale is None else descale
+    o, lse = F.fwd_fp8(q, k, v, dq, dk, dv, causal=x.causal,
+                       scale=x.scale if scale is None else scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def ulp_bf16(x):
+    return 2.0 * PT.half_ulp(x, "bf16")
+
+
+def group_trunc(q, k, chunk=16):
+    """T [B,H,R,N] (raw e4m3 values; k already repeated to q's heads): for each
+    group of 8 consecutive dimensions, the parts of its products below the step
+    2^(E-13) of the group's largest product, summed (the module docstring)."""
+    B, H, R, d = q.shape
+    N = k.shape[2]
+    aq, ak = np.abs(q), np.abs(k)
+    out = np.empty((B, H, R, N))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, R, chunk):
+                p = aq[b, h, r0:r0 + chunk, None, :] * ak[b, h, None, :, :]
+                p = p.reshape(p.shape[0], N, d // 8, 8)
+                _, e = np.frexp(p.max(-1, keepdims=True))       # max in [2^(e-1), 2^e)
+                g = np.ldexp(1.0, e - 14)
+                out[b, h, r0:r0 + chunk] = np.mod(p, g).sum((-1, -2))
+    return out
+
+
+def bounds(x, w, o_ref, rows=None):
+    """(elementwise O bound, expected squared O error, lse bound), per the module
+    docstring.  w: oracle weights [B,Hq,R,N] of the query rows `rows` (all when None)."""
+    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
+    G_ = x.Hq // x.Hkv
+    kk, vv = np.repeat(k, G_, axis=1), np.repeat(v, G_, axis=1)
+    if rows is not None:
+        q = q[:, :, rows]
+    N, d, sc = x.N, x.d, abs(x.scale)
+    dq, dk, _ = x.descale
+    q_raw = G.storage_to_f64(x.q, "e4m3")
+    if rows is not None:
+        q_raw = q_raw[:, :, rows]
+    k_raw = np.repeat(G.storage_to_f64(x.k, "e4m3"), G_, axis=1)
+    e = sc * dq * dk * group_trunc(q_raw, k_raw)                     # in-group truncation
+    e += sc * (d + 2) * U * (np.abs(q) @ np.swapaxes(np.abs(kk), -1, -2))
+    e = np.where(w > 0, e, 0.0)
+    eps = np.expm1(e) + 2.0 ** -21 + 2.0 ** -10 * (1 + 2.0 ** -4) + (N / 64 + 64) * U
+    eps = np.where(w > 0, eps, 0.0)
+    wmax = w.max(-1, keepdims=True)
+    av = np.abs(vv)
+    sys_ = (eps * w) @ av
+    b = 2.0 ** -4 * w @ av + sys_ + 2.0 ** -14 * wmax * av.sum(-2, keepdims=True)
+    b += (N * U + eps.max(-1, keepdims=True) + 2.0 ** -22) * np.abs(o_ref) + 0.5 * ulp_bf16(o_ref)
+    var = ((2.0 ** -3 * w) ** 2 / 12) @ (vv ** 2) + 2.0 ** -28 * wmax ** 2 * (vv ** 2).sum(-2, keepdims=True)
+    var += sys_ ** 2 + ulp_bf16(o_ref) ** 2 / 12
+    lse_b = PT.LSE_TOL + 2.0 * e.max(-1)
+    return b, var, lse_b
+
+
+def check(tag, o, lse, o_ref, lse_ref, b, var, lse_b):
+    assert np.isfinite(o).all(), f"{tag}: non-finite output"
+    err = np.abs(o - o_ref)
+    tol = 2.0 * b + 1e-6 * np.abs(o_ref).max()
+    worst = (err / tol).max()
+    assert worst <= 1.0, f"{tag}: max err {err.max():.3g}, worst err/bound {worst:.3f}"
+    mse, pred = (err ** 2).mean(), var.mean()
+    assert mse <= 2.0 * pred, f"{tag}: mean square error {mse:.3g} > 2 x expected {pred:.3g}"
+    lerr = np.abs(lse - lse_ref)
+    assert (lerr <= lse_b).all(), \
+        f"{tag}: lse err {lerr.max():.3g}, worst err/bound {(lerr / lse_b).max():.3f}"
+
+
+# (B, Hq, Hkv, N, d, causal, mult, scale)
+CASES = [
+    (1, 2, 2, 256, 128, True, 1.0, None),
+    (2, 4, 2, 333, 128, False, 1.0, None),
+    (1, 4, 1, 200, 64, True, 1.0, None),
+    (1, 2, 2, 1, 128, True, 1.0, None),          # one row, one key
+    (1, 2, 2, 64, 128, True, 1.0, None),         # exactly one key block
+    (1, 3, 3, 129, 128, False, 1.0, None),       # ragged tail of one key
+    (1, 2, 2, 1000, 64, False, 3.0, None),       # large scores: rescales
+    (1, 2, 1, 1024, 128, True, 1.0, -0.1),       # negative scale, GQA
+    (2, 2, 2, 700, 64, True, 2.0, 0.3),
+]
+
+
+def _id(c):
+    B, Hq, Hkv, N, d, causal, mult, scale = c
+    return f"e4m3-B{B}-H{Hq}x{Hkv}-N{N}-d{d}-{'causal' if causal else 'full'}" + \
+        (f"-x{mult:g}" if mult != 1 else "") + (f"-s{scale:g}" if scale is not None else "")
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[_id(c) for c in CASES])
+def test_fp8_parity(cfg):
+    B, Hq, Hkv, N, d, causal, mult, scale = cfg
+    x = G.make_inputs(9500 + N + d, B, Hq, Hkv, N, d, "e4m3", causal, scale=scale, mult=mult)
+    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
+    o_ref, l_ref = oracle.attention(q, k, v, causal, x.scale)
+    w = oracle.probs(q, k, causal, x.scale)
+    o, lse = run_fp8(x)
+    check(_id(cfg), o, lse, o_ref, l_ref, *bounds(x, w, o_ref))
+
+
+def test_fp8_descale_equivariance():
+    # c = |scale| dq dk log2 e is formed in double and rounded once, so halving the
+    # scale and doubling the Q descale is the same call; doubling the V descale
+    # doubles O exactly (a power of two commutes with every rounding) and leaves lse.
+    x = G.make_inputs(9601, 1, 2, 2, 300, 128, "e4m3", True)
+    dq, dk, dv = x.descale
+    o0, l0 = run_fp8(x)
+    o1, l1 = run_fp8(x, scale=x.scale / 2, descale=(dq * 2, dk, dv))
+    o2, l2 = run_fp8(x, descale=(dq, dk, dv * 2))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    assert np.array_equal(2 * o0, o2) and np.array_equal(l0, l2)
+
+
+def test_fp8_full_size_sampled_rows():
+    # The e4m3 4096-token layer (B1 H32 N4096 d128, causal) in the launch the
+    # benchmark times; the oracle checks sampled rows of three heads.
+    x = G.workload("e4m3_h32_n4096_d128_causal")
+    q, k, v = PT.to_device(x)
+    o, lse = F.fwd_fp8(q, k, v, *x.descale, causal=True, scale=x.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    rows = PT.sample_rows(x.N, 128, 61)
+    for h in (0, 13, 31):
+        qh = PT._slice64(x, "q", 0, h)
+        kh, vh = PT._slice64(x, "k", 0, h), PT._slice64(x, "v", 0, h)
+        o_ref, l_ref = oracle.attention(qh, kh, vh, True, x.scale, rows=rows)
+        w = oracle.probs(qh, kh, True, x.scale)[:, :, rows]
+        xh = G.AttentionInputs(1, 1, 1, x.N, x.d, x.dtype, True, x.scale, x.seed,
+                               x.q[:, h:h + 1], x.k[:, h:h + 1], x.v[:, h:h + 1],
+                               descale=x.descale)
+        check(f"head {h}", o[:, h:h + 1, rows], lse[:, h:h + 1, rows], o_ref, l_ref,
+              *bounds(xh, w, o_ref, rows=rows))

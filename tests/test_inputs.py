@@ -102,3 +102,44 @@ def test_make_inputs_fill_order_and_bias():
     b = G.make_inputs(1003, 2, 3, 3, 5, 4, "bf16", False, q_head_bias=True)
     assert np.array_equal(b.f64("q"), G.round_to_dtype(q + beta[None, :, None, None], "bf16"))
     assert G.make_inputs(7, 1, 1, 1, 3, 2, "f32", True).scale == float(np.float32(1 / math.sqrt(2)))
+
+
+def test_e4m3_codec_matches_torch_float8_e4m3fn():
+    # Every code decodes as torch's OCP e4m3 type does (NaN where it has NaN), and
+    # every finite value encodes back to its code (+0 and -0 distinct).
+    codes = np.arange(256, dtype=np.uint8)
+    v = G.storage_to_f64(codes, "e4m3")
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    fin = ~np.isnan(v)
+    assert np.array_equal(v[fin], t[fin])
+    assert np.array_equal(G.to_storage(v[fin], "e4m3"), codes[fin])
+    assert np.isnan(v).sum() == 2 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+
+
+def test_round_e4m3_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-5, 3, 100000)).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    x = np.concatenate([x, np.float32([2.0 ** -10, 3 * 2.0 ** -10, 1 + 2 ** -4, 1 + 3 * 2 ** -4, 232.0,
+                                       -2.0 ** -11, 0.0])])
+    r = G.round_to_dtype(x.astype(np.float64), "e4m3")
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(r, ref)
+
+
+def test_quantize_e4m3_per_tensor_descale():
+    x = G.Stream(11).normals(4096) * 3.0
+    codes, ds = G.quantize_e4m3(x)
+    vals = ds * G.storage_to_f64(codes, "e4m3")
+    assert ds == float(np.float32(np.abs(x).max() / 448.0))
+    assert np.abs(vals).max() <= 448.0 * ds * (1 + 1e-7)
+    # one rounding to e4m3 (relative 2^-4 for normals, absolute 2^-10 * ds below)
+    assert (np.abs(vals - x) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * ds) * (1 + 1e-6)).all()
+    a = G.make_inputs(21, 1, 2, 1, 50, 64, "e4m3", True)
+    assert a.q.dtype == np.uint8 and len(a.descale) == 3
+    st = G.Stream(21)
+    q = st.normals(2 * 50 * 64).reshape(1, 2, 50, 64)
+    cq, dq = G.quantize_e4m3(q)
+    assert np.array_equal(a.q, cq) and a.descale[0] == dq
+    assert np.array_equal(a.f64("q"), dq * G.storage_to_f64(cq, "e4m3"))
