@@ -5,6 +5,7 @@
     python bench.py --bwd [...]        # the backward pass (fa_bwd) on the same workload
     python bench.py --split [S] [...]  # the split-KV forward (fa_fwd_split)
     python bench.py --bias KIND [...]  # the forward with an additive bias (fa_fwd_bias)
+    python bench.py --fp8 [...]        # the e4m3-input forward (fa_fwd_fp8), same layer shape
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
 batch of seeded synthetic inputs already resident in device memory.  The default
@@ -38,17 +39,20 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (causal, d=128, N=4096)"
 METRIC_BWD = "attention bwd TFLOP/s and % of MI355X bf16 MFMA peak"
+METRIC_FP8 = "attention fwd TFLOP/s and % of MI355X fp8 MFMA peak (e4m3 inputs, causal, d=128, N=4096)"
+FP8_WORKLOAD = "e4m3_h32_n4096_d128_causal"
 BWD_FLOP_RATIO = 2.5   # backward = 5 matrix products (S, dP, dV, dK, dQ) vs the forward's 2
 DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp")
+FP8_KERNEL_SOURCES = ("fa_fp8_kernel.hpp", "fa_fwd_kernel.hpp", "fa_args.hpp")
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "io_aware_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,7 +66,8 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("kernel_sha") != kernel_sha():
+    srcs = FP8_KERNEL_SOURCES if workload.startswith("e4m3") else KERNEL_SOURCES
+    if not e or e.get("kernel_sha") != kernel_sha(srcs):
         return None
     return e.get("bytes_per_launch")
 
@@ -93,7 +98,10 @@ def cpu_baseline(x, budget_s: float = 15.0) -> dict:
     G = x.Hq // x.Hkv
 
     def f64(name, h0, h1):
-        return storage_to_f64(np.ascontiguousarray(getattr(x, name)[0:1, h0:h1]), x.dtype)
+        a = storage_to_f64(np.ascontiguousarray(getattr(x, name)[0:1, h0:h1]), x.dtype)
+        if x.descale is not None:
+            a *= x.descale["qkv".index(name)]
+        return a
 
     def row_flops(rows):
         keys = (rows + 1) if x.causal else np.full(len(rows), x.N)
@@ -164,16 +172,25 @@ def run(args) -> dict:
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
     torch.cuda.set_device(dev)
     x = G.workload(args.workload)
+    fp8 = x.dtype == "e4m3"
     tuning = G.WORKLOADS[args.workload].get("tuning")
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.dtype]
-    plan = F.plan(x.B, x.Hq, x.Hkv, x.N, x.d, x.causal, tdt, tuning=tuning, scale=x.scale)
+    if fp8:
+        plan = None
+    else:
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.dtype]
+        plan = F.plan(x.B, x.Hq, x.Hkv, x.N, x.d, x.causal, tdt, tuning=tuning, scale=x.scale)
     q, k, v = device_inputs(x, dev)
-    o = torch.empty_like(q)
+    o = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev) if fp8 else torch.empty_like(q)
     lse = torch.empty((x.B, x.Hq, x.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
         F.fwd(q, k, v, causal=x.causal, scale=x.scale, o=o, lse=lse, tuning=tuning, stream=stream)
+
+    if fp8:
+        def step():  # noqa: F811
+            F.fwd_fp8(q, k, v, *x.descale, causal=x.causal, scale=x.scale, o=o, lse=lse,
+                      stream=stream)
 
     if args.split is not None:
         S = args.split or F.split_count(x.B, x.Hq, x.N, x.causal)
@@ -241,7 +258,7 @@ def run(args) -> dict:
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Compulsory HBM bytes: Q, K, V read once; O and lse written once.  Below the
     # ridge point (peak FLOP/s / peak bytes/s) the kernel is bounded by HBM.
-    nbytes = x.q.nbytes + x.k.nbytes + x.v.nbytes + x.q.nbytes + x.B * x.Hq * x.N * 4
+    nbytes = x.q.nbytes + x.k.nbytes + x.v.nbytes + o.numel() * o.element_size() + x.B * x.Hq * x.N * 4
     peak_flops = PEAK_TFLOPS[x.dtype]
     if not args.bwd and flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
         bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
@@ -250,7 +267,7 @@ def run(args) -> dict:
         bound, unit, peak = "mfma", "TFLOP/s", peak_flops
         achieved = flops / (kernel_ms * 1e-3) / 1e12
     line = {
-        "metric": METRIC_BWD if args.bwd else METRIC,
+        "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if fp8 else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -264,7 +281,9 @@ def run(args) -> dict:
         "data": "synthetic",
         "config": {"workload": args.workload, "B": x.B, "Hq": x.Hq, "Hkv": x.Hkv, "N": x.N,
                    "d": x.d, "causal": x.causal, "scale": x.scale, "seed": x.seed,
-                   "tile": [plan.br, plan.bc], "waves": plan.waves, "grid": plan.grid},
+                   "tile": [128, 64] if fp8 else [plan.br, plan.bc],
+                   "waves": 4 if fp8 else plan.waves,
+                   "grid": x.B * x.Hq * -(-x.N // 128) if fp8 else plan.grid},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": None if args.bwd else load_traffic(args.workload),
@@ -278,6 +297,10 @@ def run(args) -> dict:
         line["config"]["pass"] = f"split-KV forward (fa_fwd_split, {S} splits: partials + merge)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
         line["roofline"]["traffic"] = None
+    if fp8:
+        line["config"]["pass"] = ("forward with e4m3 inputs and per-tensor descales (fa_fwd_fp8), "
+                                  "bf16 output")
+        line["config"]["descale"] = list(x.descale)
     if args.bwd:
         line["config"]["pass"] = "backward (fa_bwd: delta, dK/dV, dQ kernels)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
@@ -304,7 +327,13 @@ def main(argv=None) -> int:
                          "[1,Hq,N,N] or [B,Hq,N,N]")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) instead; FLOPs = 2.5x the forward's")
+    ap.add_argument("--fp8", action="store_true",
+                    help=f"time the e4m3-input forward (fa_fwd_fp8) on {FP8_WORKLOAD}")
     args = ap.parse_args(argv)
+    if args.fp8:
+        if args.bwd or args.split is not None or args.bias is not None:
+            ap.error("--fp8 times the forward pass alone")
+        args.workload = FP8_WORKLOAD
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the forward pass of one device's share is "
               f"the whole hot path here; --gpus {args.gpus} is not supported.", file=sys.stderr)

@@ -48,9 +48,11 @@ const Variant kVariants[] = {
 int elem_bytes(int dt) { return dt == FA355_F32 ? 4 : 2; }
 
 // The built-in tile (br, bc) for an input type, head dim and sequence length,
-// chosen by measurement on MI355X.  Long sequences amortise a block's loads over
-// 256 query rows; shorter ones keep 128-row tiles with 32-key blocks, whose lower
-// register use fits three wavefronts per SIMD.
+// chosen by measurement on MI355X (interleaved timings on one device).  From 4096
+// tokens at head dim 128, 256 query rows share each 64-key block (the K/V loads and
+// the per-block bookkeeping are spread over more rows: 140 us against 144 us for
+// 128 x 32 on the causal B1 H32 N4096 layer); shorter sequences keep 128-row tiles
+// with 32-key blocks, whose lower register use fits three wavefronts per SIMD.
 void default_tile(int dt, int d, int N, int &br, int &bc)
 {
     if (dt == FA355_F32) {
@@ -60,8 +62,8 @@ void default_tile(int dt, int d, int N, int &br, int &bc)
         br = 128;
         bc = 64;
     } else if (d == 128) {
-        br = N >= 8192 ? 256 : 128;
-        bc = N >= 8192 ? 64 : 32;
+        br = N >= 4096 ? 256 : 128;
+        bc = N >= 4096 ? 64 : 32;
     } else {
         br = 128;
         bc = 64;

@@ -12,9 +12,12 @@
 //      the online-softmax recurrence ("MCU 上 Transformer 模型的 Flash Attention
 //      实现…", §二, flowchart: m_new = max(m_old, rowmax S), P = exp(S - m_new),
 //      l_new = e^(m_old - m_new) l_old + rowsum P, O_new = e^(m_old - m_new) O_old + P V),
-//      in base 2 with the scale and log2(e) folded into one multiplier, and with the
-//      rescale of O and l skipped while the new block maximum stays within TAU of m
-//      (any stale m >= the true row maximum - TAU gives the same exact quotient O/l);
+//      in base 2 with the scale and log2(e) folded into one multiplier.  The quotient
+//      O/l and m + log2 l do not depend on which m is used as long as the weights
+//      stay in range, so m is only moved when it must be: the block's weights are
+//      first taken against the current m, and only if a lane's sum of them exceeds
+//      a cap (so some weight might) is the block maximum taken, O and l rescaled,
+//      and the weights recomputed;
 //   4. accumulates O^T += V_blk^T P^T on the matrix cores, P rounded to the input
 //      type; the row sum l adds those same rounded values.
 //
@@ -58,6 +61,9 @@ template <> struct Mfma<BF16> {
     // bf16 rounds P by up to 2^-8 relative, too coarse for a 1e-3 logsumexp: the
     // lse keeps its own fp32 sum of the unrounded P.
     static constexpr bool kSeparateLseSum = true;
+    // Largest lane sum of weights accepted without a rescale: bounds every weight,
+    // hence O's accumulator at N 2^16 max|V|.
+    static constexpr float kSumCap = 65536.0f;
     static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -75,6 +81,9 @@ template <> struct Mfma<BF16> {
 };
 template <> struct Mfma<F16> {
     static constexpr bool kSeparateLseSum = false;   // fp16 rounds P by <= 2^-11
+    // Weights are rounded to fp16 (largest finite 65504): a lane sum of rounded
+    // weights at most 2^15 keeps each below that (an overflow to inf fails the test).
+    static constexpr float kSumCap = 32768.0f;
     static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
@@ -417,17 +426,59 @@ fa_fwd_kernel(FwdArgs a)
                     }
             }
 
-            float mx = sacc[0][0];
+            // Weights of this block against the row maximum estimate m, packed as
+            // the B operand of P.V, with this lane's sums of them (rounded: lb;
+            // unrounded, bf16 only: leb).
+            u32x4_t pf[Tr::KS];
+            float lb = 0.0f, leb = 0.0f;
+            auto weights = [&](float m_sub) {
+                lb = 0.0f;
+                leb = 0.0f;
 #pragma unroll
-            for (int jb = 0; jb < Tr::JB; ++jb)
+                for (int jb = 0; jb < Tr::JB; ++jb) {
+                    float p[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, sacc[jb][r]);
-            const f32x2_t mp = row_pair(mx);
-            const float mt = fmaxf(mp[0], mp[1]) * c;
+                    for (int r = 0; r < 16; ++r) {
+                        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_sub));
+                        if constexpr (M::kSeparateLseSum)
+                            leb += p[r];
+                    }
+                    // The row sum adds the rounded weights the P.V product uses, so O
+                    // is an exact weighted mean of V rows with those weights.
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t pk = M::pack(p[8 * s + 2 * e], p[8 * s + 2 * e + 1]);
+                            pf[2 * jb + s][e] = pk;
+                            lb = M::sum2(pk, lb);
+                        }
+                }
+            };
 
-            if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-                const float m_new = fmaxf(m_run, mt);
+            // Any m gives the same O / l and m + log2 l, so the block maximum is only
+            // needed when the weights against the current m could grow too large.
+            // Once every row has a finite m, try the current m first: if this lane's
+            // weights sum to at most kSumCap, each of them does too (they are >= 0),
+            // and the block is done without a maximum.  A larger sum (or a non-finite
+            // one) means the block raised the row maximum: take the block maximum,
+            // rescale O and l to it and recompute the weights.
+            bool fresh = (SPLIT || BIAS) ? __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) == 0
+                                         : t != t_begin;
+            if (fresh) {
+                weights(m_run);
+                const float sum = M::kSeparateLseSum ? leb : lb;
+                fresh = __builtin_amdgcn_ballot_w64(!(sum <= M::kSumCap)) == 0;
+            }
+            if (!fresh) {
+                float mx = sacc[0][0];
+#pragma unroll
+                for (int jb = 0; jb < Tr::JB; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        mx = fmaxf(mx, sacc[jb][r]);
+                const f32x2_t mp = row_pair(mx);
+                const float m_new = fmaxf(m_run, fmaxf(mp[0], mp[1]) * c);
                 // A row that has seen no finite score yet keeps m = -inf (possible
                 // with a bias or a key-range split): nothing to scale, alpha = 1.
                 const float alpha = ((SPLIT || BIAS) && m_new == -__builtin_inff())
@@ -439,32 +490,13 @@ fa_fwd_kernel(FwdArgs a)
                 for (int nb = 0; nb < Tr::NB; ++nb)
                     oacc[nb] *= alpha;
                 m_run = m_new;
+                // Rows still without a finite score subtract 0: their weights are
+                // exp2(-inf) = 0, not NaN.
+                weights(((SPLIT || BIAS) && m_run == -__builtin_inff()) ? 0.0f : m_run);
             }
-
-            // A split's first blocks can hide every key from some rows (m = -inf):
-            // subtract 0 there, so their weights are exp2(-inf) = 0, not NaN.
-            const float m_sub = ((SPLIT || BIAS) && m_run == -__builtin_inff()) ? 0.0f : m_run;
-            u32x4_t pf[Tr::KS];
-#pragma unroll
-            for (int jb = 0; jb < Tr::JB; ++jb) {
-                float p[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_sub));
-                    if constexpr (M::kSeparateLseSum)
-                        le_part += p[r];
-                }
-                // The row sum adds the rounded weights the P.V product uses, so O is
-                // an exact weighted mean of V rows with those weights.
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t pk = M::pack(p[8 * s + 2 * e], p[8 * s + 2 * e + 1]);
-                        pf[2 * jb + s][e] = pk;
-                        l_part = M::sum2(pk, l_part);
-                    }
-            }
+            l_part += lb;
+            if constexpr (M::kSeparateLseSum)
+                le_part += leb;
 
 #pragma unroll
             for (int nb = 0; nb < Tr::NB; ++nb) {

@@ -50,10 +50,13 @@ def check(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE 
 
 def test_valid_call_plans_a_launch():
     rc, p = check(B_=1, Hq=32, Hkv=32, N=4096, d=128)
-    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 32, 4, 1024)
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (256, 64, 8, 512)
     # two stages of 16-byte slots: K rows of 16 + 1 pad slots, V rows of 16 + 2,
     # each block rounded up to whole 64-slot (1 KB) DMA instructions
     ceil64 = lambda n: (n + 63) // 64 * 64
+    assert p.lds_bytes == 2 * 16 * (ceil64(64 * 17) + ceil64(64 * 18)) == 71680
+    rc, p = check(B_=1, Hq=32, Hkv=32, N=2048, d=128)
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 32, 4, 512)
     assert p.lds_bytes == 2 * 16 * (ceil64(32 * 17) + ceil64(32 * 18)) == 36864
     rc, p = check(B_=4, Hq=32, Hkv=8, N=8192)
     assert rc == 0 and (p.br, p.bc, p.grid) == (256, 64, 4 * 32 * 32)

@@ -244,3 +244,19 @@ def test_errors_reported():
     with pytest.raises(F.FA355Error) as e:
         F.fwd(qq, qq.clone(), qq.clone(), o=qq)       # output aliases q
     assert e.value.status == -5
+
+
+@pytest.mark.parametrize("tl", [None, (128, 32), (64, 64)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_growing_row_maximum(dt, tl):
+    # Key rows scaled up along the sequence (up to 12x): in most rows the maximum
+    # score rises block after block, so the weights against the current maximum
+    # keep outgrowing the cap and the rescale path runs mid-row again and again;
+    # the weights accepted without a rescale range up to the cap (2^15 for fp16).
+    x = G.make_inputs(9400, 1, 4, 2, 700, 128, dt, True)
+    ramp = 1.0 + np.arange(x.N) / 64.0
+    k = G.to_storage(G.round_to_dtype(x.f64("k") * ramp[:, None], dt), dt)
+    x = G.AttentionInputs(x.B, x.Hq, x.Hkv, x.N, x.d, dt, True, x.scale, x.seed, x.q, k, x.v)
+    o_ref, l_ref = full_oracle(x)
+    o, l = run_gpu(x, tuning=tl)
+    PT.compare(o, l, o_ref, l_ref, dt, False, f"{dt} growing max tile{tl}")
