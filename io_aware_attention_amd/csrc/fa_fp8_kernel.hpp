@@ -24,10 +24,11 @@
 //    products of two e4m3 values are exact in fp32.
 //  * The descales fold into the score multiplier (c = |scale| dq dk log2 e) and
 //    into the output (times dv), so the matrix cores see the raw codes.
-//  * P is rounded to e4m3 for P.V.  The kernel's weights are exp2(s c - m + 4):
-//    with the lazy-rescale threshold at 4 (log2 units) they stay at or below
-//    2^8 = 256 < 448, and the prescale by 2^4 keeps weights down to 2^-10 of the
-//    running maximum in e4m3's normal range.  The row sum l adds the unrounded fp32
+//  * P is rounded to e4m3 for P.V.  The kernel's weights are exp2(s c - m + 4),
+//    m the row maximum estimate; the prescale by 2^4 keeps weights down to 2^-10 of
+//    it in e4m3's normal range.  m is moved to the block maximum only when a lane's
+//    weights sum to more than 448 (so that each stays within e4m3's range without
+//    the maximum being taken in most blocks).  The row sum l adds the unrounded fp32
 //    weights; O is normalised by it and the logsumexp is taken from it.
 //  * V is not transposed in LDS: ds_read_b64_tr_b8 gives each 16-lane group an
 //    8-key x 16-column block with lane L receiving column L % 16, so four reads
@@ -70,9 +71,9 @@ __device__ __forceinline__ int pack_fp8x4(float x0, float x1, float x2, float x3
     return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
 }
 
-template <int D>
+template <int D, int WAVES_ = 4>
 struct Fp8Traits {
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = WAVES_;
     static constexpr int BR = 32 * WAVES;        // query rows per workgroup
     static constexpr int BC = 64;                // keys per block (the MFMA's k)
     static constexpr int NT = 64 * WAVES;
@@ -84,8 +85,8 @@ struct Fp8Traits {
     static constexpr int P_INSTR = INSTR / WAVES;
     static constexpr int STAGE = 2 * BLK;
     static constexpr int LDS = 2 * STAGE;
-    static constexpr float TAU = 4.0f;           // lazy-rescale threshold, log2 units
     static constexpr float PRE = 4.0f;           // log2 of the weights' prescale
+    static constexpr float SUM_CAP = 448.0f;     // largest finite e4m3 value
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(INSTR % WAVES == 0, "whole DMA instructions per wavefront");
 
@@ -100,11 +101,11 @@ struct Fp8Traits {
     }
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, bool CAUSAL, int WAVES = 4>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 fa_fwd_fp8_kernel(FwdArgs a)
 {
-    using Tr = Fp8Traits<D>;
+    using Tr = Fp8Traits<D, WAVES>;
     constexpr int BC = Tr::BC;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -241,41 +242,54 @@ fa_fwd_fp8_kernel(FwdArgs a)
                     }
             }
 
-            float mx = sacc[0][0];
+            // Weights exp2(s c - (m - PRE)) against the row maximum estimate m,
+            // packed as the B operand of P.V (byte 16 jb + r of the lane is score
+            // register r of block jb), with this lane's sum of them.
+            i32x8_t pf;
+            float lb = 0.0f;
+            auto weights = [&](float m_sub) {
+                lb = 0.0f;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+                for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, sacc[jb][r]);
-            const f32x2_t mp = row_pair(mx);
-            const float mt = fmaxf(mp[0], mp[1]) * c;
+                    for (int g = 0; g < 4; ++g) {
+                        float p[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][4 * g + e], c, -m_sub));
+                            lb += p[e];
+                        }
+                        pf[4 * jb + g] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+                    }
+            };
 
-            if (__builtin_amdgcn_ballot_w64(mt > m_run + Tr::TAU) != 0) {
-                const float m_new = fmaxf(m_run, mt);
+            // O / l and m + log2 l do not depend on m, so the block maximum is only
+            // taken when the weights against the current m could leave e4m3's range:
+            // a lane sum of at most 448 bounds each weight by it.  After the first
+            // block every row has a finite m.
+            bool fresh = t != 0;
+            if (fresh) {
+                weights(m_run - Tr::PRE);
+                fresh = __builtin_amdgcn_ballot_w64(!(lb <= Tr::SUM_CAP)) == 0;
+            }
+            if (!fresh) {
+                float mx = sacc[0][0];
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        mx = fmaxf(mx, sacc[jb][r]);
+                const f32x2_t mp = row_pair(mx);
+                const float m_new = fmaxf(m_run, fmaxf(mp[0], mp[1]) * c);
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 l_part *= alpha;
 #pragma unroll
                 for (int nb = 0; nb < Tr::NB; ++nb)
                     oacc[nb] *= alpha;
                 m_run = m_new;
+                weights(m_run - Tr::PRE);     // each weight <= 2^PRE
             }
-
-            // Weights exp2(s c - (m - PRE)) <= 2^(TAU + PRE), packed as the B operand
-            // of P.V: byte 16 jb + r of the lane is score register r of block jb.
-            const float m_sub = m_run - Tr::PRE;
-            i32x8_t pf;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][4 * g + e], c, -m_sub));
-                        l_part += p[e];
-                    }
-                    pf[4 * jb + g] = pack_fp8x4(p[0], p[1], p[2], p[3]);
-                }
+            l_part += lb;
 
             // V^T fragments: read c gives bytes 8 c .. 8 c + 7, keys 16 c + 4 h2 +
             // {0..3, 8..11}: the keys of score registers 8 (c % 2) .. + 7 of block c / 2.
@@ -316,11 +330,11 @@ fa_fwd_fp8_kernel(FwdArgs a)
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int WAVES = 4>
 hipError_t launch_fwd_fp8_impl(const FwdArgs &a, hipStream_t stream)
 {
-    using Tr = Fp8Traits<D>;
-    const void *fn = reinterpret_cast<const void *>(&fa_fwd_fp8_kernel<D, CAUSAL>);
+    using Tr = Fp8Traits<D, WAVES>;
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_fp8_kernel<D, CAUSAL, WAVES>);
     FwdArgs arg = a;
     void *params[] = {&arg};
     return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, Tr::LDS, stream);

@@ -196,3 +196,20 @@ def test_fp8_full_size_sampled_rows():
                                descale=x.descale)
         check(f"head {h}", o[:, h:h + 1, rows], lse[:, h:h + 1, rows], o_ref, l_ref,
               *bounds(xh, w, o_ref, rows=rows))
+
+
+def test_fp8_growing_row_maximum():
+    # Key rows scaled up along the sequence (up to 12x, requantised with their own
+    # descale): the row maximum rises block after block, so the weights against the
+    # current maximum keep outgrowing the cap of 448 and the rescale path runs
+    # mid-row again and again.
+    x = G.make_inputs(9602, 1, 4, 2, 700, 128, "e4m3", True)
+    ramp = 1.0 + np.arange(x.N) / 64.0
+    k_codes, dk = G.quantize_e4m3(x.f64("k") * ramp[:, None])
+    x = G.AttentionInputs(x.B, x.Hq, x.Hkv, x.N, x.d, x.dtype, True, x.scale, x.seed, x.q,
+                          k_codes, x.v, descale=(x.descale[0], dk, x.descale[2]))
+    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
+    o_ref, l_ref = oracle.attention(q, k, v, True, x.scale)
+    w = oracle.probs(q, k, True, x.scale)
+    o, lse = run_fp8(x)
+    check("e4m3 growing max", o, lse, o_ref, l_ref, *bounds(x, w, o_ref))
