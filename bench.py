@@ -46,8 +46,9 @@ DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp")
-FP8_KERNEL_SOURCES = ("fa_fp8_kernel.hpp", "fa_fwd_kernel.hpp", "fa_args.hpp")
+# The kernel and the host code that picks its launch (tile, grid).
+KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp", "fa355.cpp")
+FP8_KERNEL_SOURCES = ("fa_fp8_kernel.hpp", "fa_fwd_kernel.hpp", "fa_args.hpp", "fa355.cpp")
 
 
 def kernel_sha(sources=KERNEL_SOURCES) -> str:

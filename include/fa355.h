@@ -187,8 +187,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
 
 /*
  * Forward with 8-bit floating-point inputs (the FP8 variant of "深度探索Flash-Attention
- * 中GQA性能调优技术解析", FP8 section, and of FlashAttention-3 in "Flash Attention là
- * gì"): q, k, v hold OCP e4m3 codes (1 sign bit, 4 exponent bits with bias 7, 3
+ * 中GQA性能调优技术解析", FP8 section, and of FlashAttention-3 in "FlashAttention
+ * (VI)", section on the evolution of the algorithm): q, k, v hold OCP e4m3 codes (1 sign bit, 4 exponent bits with bias 7, 3
  * fraction bits; largest finite 448; 0x7f and 0xff are NaN), one byte per element,
  * layouts as above.  Each tensor has one fp32 descale: the value of a stored code x
  * is descale * e4m3(x).  Computes the forward pass on those values:

@@ -5,7 +5,8 @@
 // factor: the value of a stored element x is descale * e4m3(x).  This is the FP8
 // variant of the forward pass that the GQA tuning page ("深度探索Flash-Attention中
 // GQA性能调优技术解析", FP8 section) describes as halving the memory traffic, with
-// the throughput figures of "Flash Attention là gì", section on FlashAttention-3.
+// the FP8 throughput figure of "FlashAttention (VI)", section on the evolution of
+// the algorithm, FlashAttention-3.
 // The function computed is the forward pass on the dequantised values:
 //
 //     O = softmax(scale * Qd Kd^T) Vd,   lse_i = log sum_j exp(scale * Qd_i . Kd_j),
