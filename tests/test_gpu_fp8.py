@@ -213,3 +213,17 @@ def test_fp8_growing_row_maximum():
     w = oracle.probs(q, k, True, x.scale)
     o, lse = run_fp8(x)
     check("e4m3 growing max", o, lse, o_ref, l_ref, *bounds(x, w, o_ref))
+
+
+def test_fp8_deterministic_and_gqa_bit_exact():
+    # No atomics: two runs agree bit for bit.  A K/V head shared by a group of
+    # query heads gives exactly what separate copies of it give.
+    x = G.make_inputs(9603, 2, 8, 2, 260, 128, "e4m3", True)
+    o1, l1 = run_fp8(x)
+    o2, l2 = run_fp8(x)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    y = G.AttentionInputs(x.B, x.Hq, x.Hq, x.N, x.d, x.dtype, True, x.scale, x.seed, x.q,
+                          np.ascontiguousarray(np.repeat(x.k, 4, axis=1)),
+                          np.ascontiguousarray(np.repeat(x.v, 4, axis=1)), descale=x.descale)
+    o3, l3 = run_fp8(y)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
