@@ -194,7 +194,7 @@ def run(args) -> dict:
                       stream=stream)
 
     if args.split is not None:
-        S = args.split or F.split_count(x.B, x.Hq, x.N, x.causal)
+        S = args.split or F.split_count(x.B, x.Hq, x.N, x.causal, d=x.d)
         f32 = dict(dtype=torch.float32, device=dev)
         o_part = torch.empty((S, x.B, x.Hq, x.N, x.d), **f32)
         lse_part = torch.empty((S, x.B, x.Hq, x.N), **f32)

@@ -223,9 +223,10 @@ int run_split(const void *q, const void *k, const void *v, void *o, float *lse, 
         return FA355_ERR_UNSUPPORTED;
     if (num_splits < 1 || num_splits > kMaxSplits)
         return FA355_ERR_ARG;
-    // The split kernels use 128-row query tiles: 64-key blocks at d = 64, 32-key
-    // blocks at d = 128.
-    const fa355_tuning tile = {128, d == 64 ? 64 : 32};
+    // The split kernels use 64-key blocks: 128-row query tiles at d = 64, 256-row
+    // tiles at d = 128 (measured on MI355X, B1 H2 N16384 d128 causal, 4 splits:
+    // 227 us against 244 us for 128 x 32 tiles).
+    const fa355_tuning tile = {d == 64 ? 128 : 256, 64};
     Checked c;
     int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dt, dt,
                       (d == 64 || d == 128) ? &tile : nullptr, c);
@@ -261,10 +262,10 @@ int run_split(const void *q, const void *k, const void *v, void *o, float *lse, 
 
 #define FA355_BIAS_ROW(T, D, BC, W, C) {FA355_DT_##T, D, BC, C, &fa355::launch_fwd_bias<fa355::T, D, BC, W, C>},
 const SplitVariant kBiasVariants[] = {
-    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, BF16, 64)
-    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, BF16, 128)
-    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, F16, 64)
-    FA355_SPLIT_VARIANTS(FA355_BIAS_ROW, F16, 128)
+    FA355_BIAS_VARIANTS(FA355_BIAS_ROW, BF16, 64)
+    FA355_BIAS_VARIANTS(FA355_BIAS_ROW, BF16, 128)
+    FA355_BIAS_VARIANTS(FA355_BIAS_ROW, F16, 64)
+    FA355_BIAS_VARIANTS(FA355_BIAS_ROW, F16, 128)
 };
 
 int run_bias(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -112,6 +112,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 // Backward variants: Z(T, D, CAUSAL), 16-bit inputs, head dims 64 and 128.
 #define FA355_BWD_VARIANTS(Z, T) Z(T, 64, false) Z(T, 64, true) Z(T, 128, false) Z(T, 128, true)
 
-// Split-KV variants: S(T, D, BC, WAVES, CAUSAL).
+// Split-KV variants: S(T, D, BC, WAVES, CAUSAL): 64-key blocks, 128-row tiles at
+// head dim 64 and 256-row tiles at 128.
 #define FA355_SPLIT_VARIANTS(S, T, D)                                                 \
+    S(T, D, 64, (D == 64 ? 4 : 8), false) S(T, D, 64, (D == 64 ? 4 : 8), true)
+
+// Additive-bias variants, same signature: 128-row tiles, 64-key blocks at head dim
+// 64 and 32-key blocks at 128 (the bias tile shares the LDS stage with K and V).
+#define FA355_BIAS_VARIANTS(S, T, D)                                                  \
     S(T, D, (D == 64 ? 64 : 32), 4, false) S(T, D, (D == 64 ? 64 : 32), 4, true)

@@ -181,3 +181,16 @@ def fp8_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BA
 ])
 def test_fp8_rejections(kw, code):
     assert fp8_call(**kw) == code, kw
+
+
+def test_split_count_heuristic():
+    # About two 256-row workgroups per CU at head dim 128, four 128-row ones at 64,
+    # at least four 64-key blocks per split, never above 16, 1 when the tiles
+    # already fill the GPU.
+    assert F.split_count(1, 2, 16384, True) == 4
+    assert F.split_count(1, 2, 16384, True, d=64) == 4
+    assert F.split_count(1, 32, 4096, True) == 1
+    assert F.split_count(1, 1, 64, True) == 1
+    assert F.split_count(1, 1, 8192, True) == 16        # 32 tiles: capped at 16
+    assert F.split_count(1, 1, 1 << 20, True) == 1      # 4096 tiles fill the GPU
+    assert F.split_count(1, 1, 1024, False) == 4     # 16 key blocks: at most 4 splits

@@ -53,12 +53,13 @@ def test_split_parity(cfg):
 
 
 def test_split_matches_unsplit_within_rounding():
-    # One split is the forward pass with an extra fp32 round trip through the
-    # workspace: the two outputs differ at most by the output rounding.
+    # One split is the forward pass (same 256 x 64 tiles at head dim 128) with an
+    # extra fp32 round trip through the workspace: the two outputs differ at most
+    # by the output rounding.
     x = G.make_inputs(9950, 1, 4, 4, 600, 128, "bf16", True)
     q, k, v = PT.to_device(x)
     o1, l1 = F.fwd_split(q, k, v, causal=True, scale=x.scale, num_splits=1)
-    o0, l0 = F.fwd(q, k, v, causal=True, scale=x.scale, tuning=(128, 32))
+    o0, l0 = F.fwd(q, k, v, causal=True, scale=x.scale, tuning=(256, 64))
     torch.cuda.synchronize()
     a, b = o0.float().cpu().double().numpy(), o1.float().cpu().double().numpy()
     assert np.abs(a - b).max() <= PT.half_ulp(a, "bf16").max() * 2
