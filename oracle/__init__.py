@@ -9,6 +9,7 @@ Two independent C implementations sit behind these wrappers:
 
 * ``attention`` / ``probs`` -- the plain definition softmax(Q K^T * scale) V with a
   two-pass softmax over materialised score rows (attention_oracle.c);
+  ``attention_kv`` the same for queries against a longer key/value sequence;
 * ``blocked`` -- the tiled online-softmax merge equations, key/value blocks outer,
   query blocks inner, per-row state (blocked_reference.c);
 * ``grads`` -- dQ, dK, dV of the plain definition by the chain rule, one softmax
@@ -58,6 +59,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.oracle_attention_fwd_bias.argtypes = [dp, dp, dp, dp, i64, i64, i64, dp, dp, i64, i64,
                                               i64, i64, i64, ip, ctypes.c_double, ip]
     lib.oracle_attention_fwd_bias.restype = ip
+    lib.oracle_attention_fwd_kv.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+                                            ip, ctypes.c_double, ip]
+    lib.oracle_attention_fwd_kv.restype = ip
     lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                          ip, ctypes.c_double, ip]
     lib.oracle_attention_bwd.restype = ip
@@ -110,6 +114,28 @@ def attention(q, k, v, causal: bool, scale: float, rows=None, threads: int = 0,
                                 _ptr(r), R, int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attention_fwd failed with {rc}")
+    return o, lse
+
+
+def attention_kv(q, k, v, causal: bool, scale: float, threads: int = 0, lib=None):
+    """Exact attention of Nq queries against Nk keys/values (decoding with a cache).
+
+    q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]; when causal, Nq <= Nk and query i sees keys
+    j <= i + Nk - Nq (the queries are the last Nq positions).  Returns (o, lse).
+    """
+    L = _get(lib)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    o = np.empty((B, Hq, Nq, d), np.float64)
+    lse = np.empty((B, Hq, Nq), np.float64)
+    rc = L.oracle_attention_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                   int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_fwd_kv failed with {rc}")
     return o, lse
 
 

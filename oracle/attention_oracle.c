@@ -34,6 +34,12 @@
  * Layouts: q, o are [B,Hq,N,d]; k, v are [B,Hkv,N,d]; lse is [B,Hq,N]; all fp64,
  * contiguous, d innermost.  With a row list, o and lse hold only those rows, in
  * list order: o is [B,Hq,nrows,d], lse is [B,Hq,nrows].
+ *
+ * Queries against a longer key/value sequence (decoding with a key/value cache,
+ * oracle_attention_fwd_kv): q, o are [B,Hq,Nq,d], k, v are [B,Hkv,Nk,d], Nq <= Nk
+ * when causal.  Reading (the pages only treat square causal attention): the Nq
+ * queries are the last Nq of the Nk positions, so query i sees keys
+ * j <= i + (Nk - Nq); for Nq = Nk this is the square rule j <= i.
  */
 #include <math.h>
 #include <pthread.h>
@@ -45,7 +51,8 @@
 typedef struct {
     const double *q, *k, *v;
     double *o, *lse, *probs;
-    int64_t B, Hq, Hkv, N, d;
+    int64_t B, Hq, Hkv, N, d;  /* N: query rows per head                            */
+    int64_t Nk;                /* key/value rows per head (N for square attention)  */
     int causal;
     double scale;
     const double *bias;    /* optional additive bias, element (b,h,i,j) at       */
@@ -72,18 +79,19 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
     const int64_t b = bh / J->Hq, h = bh % J->Hq;
     const int64_t group = J->Hq / J->Hkv;
     const int64_t hk = h / group;
-    const int64_t N = J->N, d = J->d;
+    const int64_t N = J->N, Nk = J->Nk, d = J->d;
     const int64_t r0 = (unit % J->units_per_bh) * J->chunk;
     const int64_t r1 = (r0 + J->chunk < J->nrows) ? r0 + J->chunk : J->nrows;
 
     const double *qh = J->q + (b * J->Hq + h) * N * d;
-    const double *kh = J->k + (b * J->Hkv + hk) * N * d;
-    const double *vh = J->v + (b * J->Hkv + hk) * N * d;
+    const double *kh = J->k + (b * J->Hkv + hk) * Nk * d;
+    const double *vh = J->v + (b * J->Hkv + hk) * Nk * d;
 
     for (int64_t r = r0; r < r1; ++r) {
         const int64_t i = row_index(J, r);
-        const int64_t jend = J->causal ? i + 1 : N;   /* visible keys: j < jend */
-        double *s = S + (r - r0) * N;
+        /* Visible keys: j < jend (query i is position i + Nk - N of the keys). */
+        const int64_t jend = J->causal ? i + 1 + (Nk - N) : Nk;
+        double *s = S + (r - r0) * Nk;
         const double *qi = qh + i * d;
 
         /* Scores s_ij = scale * sum_t q_it k_jt (+ bias), the full row materialised. */
@@ -128,8 +136,8 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
         if (J->lse)
             J->lse[bh * J->nrows + r] = l > 0.0 ? m + log(l) : -INFINITY;
         if (J->probs) {
-            double *pr = J->probs + (bh * J->nrows + r) * N;
-            for (int64_t j = 0; j < N; ++j)
+            double *pr = J->probs + (bh * J->nrows + r) * Nk;
+            for (int64_t j = 0; j < Nk; ++j)
                 pr[j] = j < jend ? s[j] : 0.0;
         }
     }
@@ -138,7 +146,7 @@ static void run_unit(const oracle_job *J, int64_t unit, double *S)
 static void *worker(void *arg)
 {
     oracle_job *J = (oracle_job *)arg;
-    double *S = (double *)malloc((size_t)(J->chunk * J->N) * sizeof(double));
+    double *S = (double *)malloc((size_t)(J->chunk * J->Nk) * sizeof(double));
     if (!S) {
         pthread_mutex_lock(&J->mu);
         J->failed = 1;
@@ -169,7 +177,7 @@ static int run_job(oracle_job *J, int threads)
     const int64_t heads = J->B * J->Hq;
     const int64_t want = (4LL * threads + heads - 1) / heads;
     int64_t chunk = (J->nrows + want - 1) / want;
-    const int64_t cap = (64LL << 20) / (8 * J->N);
+    const int64_t cap = (64LL << 20) / (8 * J->Nk);
     if (chunk > cap)
         chunk = cap;
     if (chunk < 1)
@@ -238,7 +246,7 @@ int oracle_attention_fwd(const double *q, const double *k, const double *v,
     oracle_job J;
     memset(&J, 0, sizeof(J));
     J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.probs = NULL;
-    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.Nk = N; J.d = d;
     J.causal = causal != 0;
     J.scale = scale;
     J.rows = rows;
@@ -262,7 +270,7 @@ int oracle_attention_probs(const double *q, const double *k, double *probs,
     oracle_job J;
     memset(&J, 0, sizeof(J));
     J.q = q; J.k = k; J.v = k; J.o = NULL; J.lse = NULL; J.probs = probs;
-    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.Nk = N; J.d = d;
     J.causal = causal != 0;
     J.scale = scale;
     J.rows = NULL;
@@ -289,10 +297,38 @@ int oracle_attention_fwd_bias(const double *q, const double *k, const double *v,
     memset(&J, 0, sizeof(J));
     J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.probs = NULL;
     J.bias = bias; J.sb = sb; J.sh = sh; J.si = si;
-    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.Nk = N; J.d = d;
     J.causal = causal != 0;
     J.scale = scale;
     J.rows = NULL;
     J.nrows = N;
+    return run_job(&J, threads);
+}
+
+/*
+ * Queries against a key/value sequence of another length (see the header): q, o
+ * [B,Hq,Nq,d], k, v [B,Hkv,Nk,d], lse [B,Hq,Nq]; causal requires Nq <= Nk.  Returns
+ * as oracle_attention_fwd.
+ */
+int oracle_attention_fwd_kv(const double *q, const double *k, const double *v,
+                            double *o, double *lse,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                            int causal, double scale, int threads)
+{
+    if (!q || !k || !v)
+        return -1;
+    int rc = check_args(B, Hq, Hkv, Nq, d, NULL, Nq);
+    if (rc)
+        return rc;
+    if (Nk < 1 || (causal && Nq > Nk))
+        return -2;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.o = o; J.lse = lse; J.probs = NULL;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = Nq; J.Nk = Nk; J.d = d;
+    J.causal = causal != 0;
+    J.scale = scale;
+    J.rows = NULL;
+    J.nrows = Nq;
     return run_job(&J, threads);
 }

@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle_pins as P
 import grad_pins as GP
+import decode_pins as DP
 import bias_pins as BP
 
 ORACLE = "attention_oracle.c"
@@ -20,8 +21,9 @@ GRAD = "attention_grad_oracle.c"
 
 # (id, file, [(original, replacement), ...])
 MUTANTS = [
-    ("causal_strict", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i : N")]),
-    ("causal_leak", ORACLE, [("J->causal ? i + 1 : N", "J->causal ? i + 2 : N")]),
+    ("causal_strict", ORACLE, [("J->causal ? i + 1 + (Nk - N) : Nk", "J->causal ? i + (Nk - N) : Nk")]),
+    ("causal_leak", ORACLE, [("J->causal ? i + 1 + (Nk - N) : Nk", "J->causal ? i + 2 + (Nk - N) : Nk")]),
+    ("cache_offset_dropped", ORACLE, [("J->causal ? i + 1 + (Nk - N) : Nk", "J->causal ? i + 1 : Nk")]),
     ("gqa_modulo", ORACLE, [("const int64_t hk = h / group;", "const int64_t hk = h % J->Hkv;")]),
     ("exp_sign", ORACLE, [("exp(s[j] - m);", "exp(m - s[j]);")]),
     ("no_scale", ORACLE, [("s[j] = J->scale * acc;", "s[j] = acc;")]),
@@ -34,8 +36,8 @@ MUTANTS = [
     ("lse_without_max", ORACLE, [("? m + log(l) :", "? log(l) :")]),
     ("dot_skips_last", ORACLE, [("for (int64_t t = 0; t < d; ++t)\n                acc += qi[t] * kj[t];",
                                  "for (int64_t t = 0; t + 1 < d; ++t)\n                acc += qi[t] * kj[t];")]),
-    ("key_head_not_query_head", ORACLE, [("const double *kh = J->k + (b * J->Hkv + hk) * N * d;",
-                                          "const double *kh = J->k + (b * J->Hkv + h % J->Hkv) * N * d;")]),
+    ("key_head_not_query_head", ORACLE, [("const double *kh = J->k + (b * J->Hkv + hk) * Nk * d;",
+                                          "const double *kh = J->k + (b * J->Hkv + h % J->Hkv) * Nk * d;")]),
     ("blocked_no_rescale_l", BLOCKED, [("l[i] = a_old * l[i] + a_blk * lt;", "l[i] = l[i] + a_blk * lt;")]),
     ("blocked_no_rescale_o", BLOCKED, [("acc[i * d + t] = a_old * acc[i * d + t] + a_blk * pv[t];",
                                         "acc[i * d + t] = acc[i * d + t] + a_blk * pv[t];")]),
@@ -67,6 +69,7 @@ def _quick_oracle_pins(lib):
     P.pin_closed_forms(lib)
     P.pin_invariants(lib)
     BP.all_bias_pins(lib)
+    DP.all_decode_pins(lib)
 
 
 def _quick_grad_pins(lib):
