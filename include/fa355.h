@@ -206,6 +206,31 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                float q_descale, float k_descale, float v_descale, hipStream_t stream);
 
+/*
+ * Decoding against a key/value cache: Nq new queries per head against Nk cached
+ * keys and values, for Nq much smaller than Nk.
+ *   q, o       device pointers [B,Hq,Nq,d], element type `dtype`
+ *   k, v       device pointers [B,Hkv,Nk,d]
+ *   lse        device pointer [B,Hq,Nq] fp32, or NULL
+ *   causal     nonzero: the queries are the last Nq of the Nk positions, so query i
+ *              sees keys j <= i + Nk - Nq (requires Nq <= Nk, else FA355_ERR_SHAPE);
+ *              zero: every query sees every key
+ *   dtype      F16 or BF16; d in {64, 128}
+ *   num_splits 1 .. 256 pieces of the key range, each handled by its own workgroup
+ *   o_part     caller-owned fp32 workspace [num_splits,B,Hq,Nq,d]
+ *   lse_part   caller-owned fp32 workspace [num_splits,B,Hq,Nq]
+ * The Hq/Hkv query heads that share a K/V head are computed together, their
+ * (Hq/Hkv)*Nq (head, query) rows packed into one 32-row tile (the PackGQA scheme of
+ * "深度探索Flash-Attention中GQA性能调优技术解析", PackGQA section), so
+ * (Hq/Hkv)*Nq <= 32 is required (else FA355_ERR_UNSUPPORTED).  Partial results over
+ * the key pieces merge exactly as in fa_fwd_split.  Enqueues two kernels on
+ * `stream`; allocates nothing; validation as for fa_fwd_split.
+ */
+int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                  fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
+                  hipStream_t stream);
+
 /* A static, human-readable name for a status code ("unknown status" otherwise). */
 const char *fa_status_str(int status);
 

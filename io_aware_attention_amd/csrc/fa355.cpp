@@ -472,6 +472,99 @@ int run_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
     return e == hipSuccess ? FA355_OK : FA355_ERR_HIP;
 }
 
+constexpr int kMaxDecodeSplits = 256;
+
+int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dt,
+               int num_splits, float *o_part, float *lse_part, hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !o_part || !lse_part)
+        return FA355_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0 || (causal && Nq > Nk))
+        return FA355_ERR_SHAPE;
+    if ((dt != FA355_F16 && dt != FA355_BF16) || (d != 64 && d != 128))
+        return FA355_ERR_UNSUPPORTED;
+    // The (head, query) rows of one K/V group must fit one wavefront's 32 rows.
+    const int group = Hq / Hkv;
+    if ((int64_t)group * Nq > 32)
+        return FA355_ERR_UNSUPPORTED;
+    // One K/V head plus one block past its end in 32-bit byte offsets.
+    if (((int64_t)Nk + 32) * d * 2 > INT_MAX - 65536)
+        return FA355_ERR_SHAPE;
+    if (!std::isfinite(scale))
+        return FA355_ERR_ARG;
+    if (num_splits < 1 || num_splits > kMaxDecodeSplits)
+        return FA355_ERR_ARG;
+    const void *al16[] = {q, k, v, o, o_part};
+    for (const void *p : al16)
+        if (reinterpret_cast<uintptr_t>(p) % 16)
+            return FA355_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(lse_part) % 4)
+        return FA355_ERR_ALIGN;
+    const size_t rows = (size_t)B * Hq * Nq;
+    const size_t nq = rows * d * 2, nkv = (size_t)B * Hkv * Nk * d * 2;
+    const size_t bp = (size_t)num_splits * rows * d * 4, bl = (size_t)num_splits * rows * 4;
+    struct Span { const void *p; size_t n; };
+    const Span in[] = {{q, nq}, {k, nkv}, {v, nkv}};
+    const Span out[] = {{o, nq}, {lse, lse ? rows * 4 : 0}, {o_part, bp}, {lse_part, bl}};
+    for (size_t x = 0; x < 4; ++x) {
+        for (const Span &i : in)
+            if (overlaps(out[x].p, out[x].n, i.p, i.n))
+                return FA355_ERR_ARG;
+        for (size_t y = x + 1; y < 4; ++y)
+            if (overlaps(out[x].p, out[x].n, out[y].p, out[y].n))
+                return FA355_ERR_ARG;
+    }
+    if ((int64_t)B * Hkv * num_splits > INT_MAX || (int64_t)rows > INT_MAX)
+        return FA355_ERR_SHAPE;
+
+    float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+    if (!(c >= 1.17549435e-38f))
+        c = 1.17549435e-38f;
+    fa355::DecodeArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.group = group;
+    a.rows = group * Nq;
+    a.num_splits = num_splits;
+    const int n_blk = (Nk + 31) / 32;
+    a.blocks_per_split = (n_blk + num_splits - 1) / num_splits;
+    a.c = c;
+    a.q_sign = scale < 0.0f ? 0x80008000u : 0u;
+    // The merge kernel sees the queries as a [B, Hq, Nq] problem.
+    fa355::FwdArgs m = {};
+    m.o = o;
+    m.lse = lse;
+    m.B = B;
+    m.Hq = Hq;
+    m.Hkv = Hkv;
+    m.N = Nq;
+    m.num_splits = num_splits;
+    m.o_part = o_part;
+    m.lse_part = lse_part;
+    hipError_t e;
+    const bool cz = causal != 0, bf = dt == FA355_BF16;
+    if (d == 64)
+        e = bf ? (cz ? fa355::launch_decode<fa355::BF16, 64, true>(a, m, stream)
+                     : fa355::launch_decode<fa355::BF16, 64, false>(a, m, stream))
+               : (cz ? fa355::launch_decode<fa355::F16, 64, true>(a, m, stream)
+                     : fa355::launch_decode<fa355::F16, 64, false>(a, m, stream));
+    else
+        e = bf ? (cz ? fa355::launch_decode<fa355::BF16, 128, true>(a, m, stream)
+                     : fa355::launch_decode<fa355::BF16, 128, false>(a, m, stream))
+               : (cz ? fa355::launch_decode<fa355::F16, 128, true>(a, m, stream)
+                     : fa355::launch_decode<fa355::F16, 128, false>(a, m, stream));
+    return e == hipSuccess ? FA355_OK : FA355_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,6 +647,15 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                    v_descale, stream);
 }
 
-int fa_version(void) { return 140; }
+int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                  fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
+                  hipStream_t stream)
+{
+    return run_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
+                      o_part, lse_part, stream);
+}
+
+int fa_version(void) { return 150; }
 
 }  // extern "C"

@@ -83,6 +83,22 @@ hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream);
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_fp8(const FwdArgs &a, hipStream_t stream);
 
+// Decoding against a key/value cache: the packed-group kernel over num_splits key
+// ranges, then the merge kernel (fa_decode_kernel.hpp).
+struct DecodeArgs {
+    const void *q, *k, *v;
+    float *o_part, *lse_part;      // [S, B, Hq, Nq, D] and [S, B, Hq, Nq]
+    int B, Hq, Hkv, Nq, Nk;
+    int group;                     // Hq / Hkv
+    int rows;                      // group * Nq <= 32
+    int num_splits;
+    int blocks_per_split;          // 32-key blocks per piece
+    float c;                       // |scale| log2(e)
+    uint32_t q_sign;               // 0x80008000 flips every 16-bit Q element
+};
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_decode(const DecodeArgs &a, const FwdArgs &merge, hipStream_t stream);
+
 // The three backward kernels (delta, dK/dV, dQ), in order on `stream`.
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);

@@ -21,7 +21,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -
 
 # Every exported symbol, as declared in include/fa355.h.
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_fwd_bias", "fa_bwd",
-           "fa_fwd_fp8", "fa_status_str", "fa_version")
+           "fa_fwd_fp8", "fa_fwd_decode", "fa_status_str", "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = ip
     L.fa_fwd_fp8.argtypes = common + [fp, fp, fp, vp]
     L.fa_fwd_fp8.restype = ip
+    L.fa_fwd_decode.argtypes = [vp] * 5 + [ip] * 7 + [fp, ip, ip, vp, vp, vp]
+    L.fa_fwd_decode.restype = ip
     L.fa_status_str.argtypes = [ip]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -320,5 +322,49 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
     rc = L.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), float(q_descale),
                       float(k_descale), float(v_descale), ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse
+
+
+def decode_split_count(B: int, Hkv: int, Nk: int, cus: int = 256) -> int:
+    """Key-range pieces for fwd_decode: about eight single-wavefront workgroups per
+    compute unit, each piece at least four 32-key blocks, at most 256 pieces."""
+    want = -(-8 * cus // (B * Hkv))
+    blocks = (Nk + 31) // 32
+    return max(1, min(256, want, blocks // 4))
+
+
+def fwd_decode(q, k, v, causal: bool = True, scale: float | None = None, num_splits=None, *,
+               o=None, lse=None, o_part=None, lse_part=None, stream=None):
+    """Decoding against a key/value cache: returns (o, lse).
+
+    q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d] (the cache, new positions included); one
+    16-bit dtype, d = 64 or 128, (Hq/Hkv)*Nq <= 32.  causal: query i sees keys
+    j <= i + Nk - Nq.  num_splits defaults to decode_split_count(); the fp32
+    workspaces are allocated with torch unless given.
+    """
+    import torch
+    L = lib()
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    S = int(decode_split_count(B, Hkv, Nk) if num_splits is None else num_splits)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Nq), **f32) if lse is None else lse
+    o_part = torch.empty((S, B, Hq, Nq, d), **f32) if o_part is None else o_part
+    lse_part = torch.empty((S, B, Hq, Nq), **f32) if lse_part is None else lse_part
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), _dtype_code(q.dtype),
+                         S, o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return o, lse

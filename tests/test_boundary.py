@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = F.lib()
-    assert L.fa_version() == 140
+    assert L.fa_version() == 150
     for s in range(-6, 1):
         assert F.status_str(s) and F.status_str(s) != "unknown status"
     assert F.status_str(-99) == "unknown status"
@@ -194,3 +194,29 @@ def test_split_count_heuristic():
     assert F.split_count(1, 1, 8192, True) == 16        # 32 tiles: capped at 16
     assert F.split_count(1, 1, 1 << 20, True) == 1      # 4096 tiles fill the GPU
     assert F.split_count(1, 1, 1024, False) == 4     # 16 key blocks: at most 4 splits
+
+
+def decode_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+                B_=1, Hq=8, Hkv=2, Nq=2, Nk=100, d=128, causal=1, scale=0.1, dt=F.BF16, S=4,
+                op=BASE + 5 * SPAN, lp=BASE + 6 * SPAN):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_fwd_decode(q, k, v, o, lse, B_, Hq, Hkv, Nq, Nk, d, causal, scale, dt, S,
+                                 op, lp, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1), (dict(o=None), -1),
+    (dict(B_=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(Hq=3), -2),
+    (dict(Nq=101), -2), (dict(Nk=1 << 30), -2),
+    (dict(Nq=9), -3), (dict(Hq=64, Hkv=1, Nq=1), -3), (dict(d=256), -3), (dict(dt=F.F32, d=64), -3),
+    (dict(S=0), -5), (dict(S=257), -5), (dict(scale=float("nan")), -5),
+    (dict(q=BASE + 8), -4), (dict(op=BASE + 5 * SPAN + 4), -4), (dict(lse=BASE + 4 * SPAN + 2), -4),
+    (dict(o=BASE + 64), -5), (dict(op=BASE + 3 * SPAN + 64), -5), (dict(lp=BASE + 5 * SPAN + 16), -5),
+])
+def test_decode_rejections(kw, code):
+    assert decode_call(**kw) == code, kw
+
+
+def test_decode_allows_more_queries_than_keys_without_causal_mask():
+    # Nq > Nk is only an error under the causal mask (checked before any HIP call).
+    assert decode_call(Nq=2, Nk=1, S=0, causal=0) == -5
