@@ -6,6 +6,7 @@
     python bench.py --split [S] [...]  # the split-KV forward (fa_fwd_split)
     python bench.py --bias KIND [...]  # the forward with an additive bias (fa_fwd_bias)
     python bench.py --fp8 [...]        # the e4m3-input forward (fa_fwd_fp8), same layer shape
+    python bench.py --decode [...]     # decoding against a key/value cache (fa_fwd_decode)
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
 batch of seeded synthetic inputs already resident in device memory.  The default
@@ -41,6 +42,10 @@ METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (causal, d=128, N
 METRIC_BWD = "attention bwd TFLOP/s and % of MI355X bf16 MFMA peak"
 METRIC_FP8 = "attention fwd TFLOP/s and % of MI355X fp8 MFMA peak (e4m3 inputs, causal, d=128, N=4096)"
 FP8_WORKLOAD = "e4m3_h32_n4096_d128_causal"
+METRIC_DECODE = "attention decode GB/s (K/V cache read) and % of MI355X HBM bandwidth"
+DECODE_WORKLOAD = "bf16_decode_b8_hq32_hkv8_nk8192_d128"
+DECODE_KERNEL_SOURCES = ("fa_decode_kernel.hpp", "fa_fwd_kernel.hpp", "fa_inst_decode.hip",
+                         "fa_args.hpp", "fa355.cpp")
 BWD_FLOP_RATIO = 2.5   # backward = 5 matrix products (S, dP, dV, dK, dQ) vs the forward's 2
 DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
@@ -67,7 +72,8 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    srcs = FP8_KERNEL_SOURCES if workload.startswith("e4m3") else KERNEL_SOURCES
+    srcs = (FP8_KERNEL_SOURCES if workload.startswith("e4m3") else
+            DECODE_KERNEL_SOURCES if "decode" in workload else KERNEL_SOURCES)
     if not e or e.get("kernel_sha") != kernel_sha(srcs):
         return None
     return e.get("bytes_per_launch")
@@ -162,6 +168,106 @@ def cpu_baseline_bwd(x, budget_s: float) -> dict:
             "kind": "oracle",
             "sample": f"all {x.N} rows of heads 0..{nh - 1} (batch 0) of {x.recipe}, gradients; "
                       f"{dt:.1f} s in fp64 on {min(threads, groups)} threads"}
+
+
+def decode_bytes(x) -> int:
+    """Compulsory HBM bytes of one decode call: the K/V cache and Q read once, O and
+    lse written once (the split workspace is not counted)."""
+    e = 2
+    return (2 * x.B * x.Hkv * x.Nk * x.d * e + 2 * x.B * x.Hq * x.Nq * x.d * e
+            + 4 * x.B * x.Hq * x.Nq)
+
+
+def cpu_baseline_decode(x) -> dict:
+    """The fp64 oracle, as it stands, on the whole decode workload, in GB/s of the
+    same compulsory bytes."""
+    import oracle
+    from fa_inputs import storage_to_f64
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    q, k, v = (storage_to_f64(getattr(x, n), x.dtype) for n in "qkv")
+    t0 = time.perf_counter()
+    oracle.attention_kv(q, k, v, x.causal, x.scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": decode_bytes(x) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {x.recipe} workload; {dt:.2f} s in fp64 on {threads} threads"}
+
+
+def run_decode(args) -> dict:
+    import torch
+
+    import fa_inputs as G
+    import io_aware_attention_amd as F
+
+    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
+    torch.cuda.set_device(dev)
+    x = G.workload(args.workload)
+    q, k, v = device_inputs(x, dev)
+    S = args.split or F.decode_split_count(x.B, x.Hkv, x.Nk)
+    o = torch.empty_like(q)
+    lse = torch.empty((x.B, x.Hq, x.Nq), dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_part = torch.empty((S, x.B, x.Hq, x.Nq, x.d), **f32)
+    lse_part = torch.empty((S, x.B, x.Hq, x.Nq), **f32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        F.fwd_decode(q, k, v, causal=x.causal, scale=x.scale, num_splits=S, o=o, lse=lse,
+                     o_part=o_part, lse_part=lse_part, stream=stream)
+
+    if args.profile_run:
+        for _ in range(3):
+            step()
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"profile_run": args.workload, "copy_bytes": src.numel() * 4}), flush=True)
+        return {}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = e0.elapsed_time(e1) / args.steps
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output")
+    nbytes = decode_bytes(x)
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_DECODE,
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": x.B, "Hq": x.Hq, "Hkv": x.Hkv, "Nq": x.Nq,
+                   "Nk": x.Nk, "d": x.d, "causal": x.causal, "scale": x.scale, "seed": x.seed,
+                   "num_splits": S, "bytes": nbytes, "flops": x.flops,
+                   "pass": "decoding against a key/value cache (fa_fwd_decode: packed "
+                           "query-head groups over key pieces, then the merge kernel)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic(args.workload),
+                     "kernel_us": round(kernel_ms * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_decode(x)
+    return line
 
 
 def run(args) -> dict:
@@ -328,6 +434,9 @@ def main(argv=None) -> int:
                          "[1,Hq,N,N] or [B,Hq,N,N]")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) instead; FLOPs = 2.5x the forward's")
+    ap.add_argument("--decode", action="store_true",
+                    help=f"time decoding against a key/value cache (fa_fwd_decode) on "
+                         f"{DECODE_WORKLOAD} (--split sets the key pieces)")
     ap.add_argument("--fp8", action="store_true",
                     help=f"time the e4m3-input forward (fa_fwd_fp8) on {FP8_WORKLOAD}")
     args = ap.parse_args(argv)
@@ -341,7 +450,12 @@ def main(argv=None) -> int:
         return 2
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
-    line = run(args)
+    if args.decode:
+        if args.bwd or args.fp8 or args.bias is not None:
+            ap.error("--decode times the decoding call alone")
+        if args.workload == DEFAULT_WORKLOAD:
+            args.workload = DECODE_WORKLOAD
+    line = run_decode(args) if args.decode else run(args)
     if line:
         print(json.dumps(line), flush=True)
     return 0

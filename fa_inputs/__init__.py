@@ -41,6 +41,7 @@ import numpy as np
 __all__ = [
     "splitmix64", "Stream", "round_to_dtype", "to_storage", "storage_to_f64",
     "AttentionInputs", "make_inputs", "WORKLOADS", "workload", "quantize_e4m3",
+    "DecodeInputs", "make_decode_inputs", "DECODE_WORKLOADS",
 ]
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -341,8 +342,65 @@ WORKLOADS = {
 }
 
 
-def workload(name: str) -> AttentionInputs:
+@dataclass
+class DecodeInputs:
+    """Nq new queries per head against an Nk-row key/value cache (storage arrays)."""
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    seed: int
+    q: np.ndarray         # [B, Hq, Nq, d]
+    k: np.ndarray         # [B, Hkv, Nk, d]
+    v: np.ndarray
+    recipe: str = ""
+
+    def f64(self, name: str) -> np.ndarray:
+        return storage_to_f64(getattr(self, name), self.dtype)
+
+    @property
+    def flops(self) -> float:
+        """4*d per visible (query, key) pair."""
+        if self.causal:
+            pairs = sum(self.Nk - self.Nq + i + 1 for i in range(self.Nq))
+        else:
+            pairs = self.Nq * self.Nk
+        return 4.0 * self.B * self.Hq * pairs * self.d
+
+
+def make_decode_inputs(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                       dtype: str, causal: bool = True, scale: float | None = None,
+                       recipe: str = "") -> DecodeInputs:
+    """Draw Q, then K, then V (normal, row-major) and round each once to dtype."""
+    st = Stream(seed)
+    q = st.normals(B * Hq * Nq * d).reshape(B, Hq, Nq, d)
+    k = st.normals(B * Hkv * Nk * d).reshape(B, Hkv, Nk, d)
+    v = st.normals(B * Hkv * Nk * d).reshape(B, Hkv, Nk, d)
+    out = [to_storage(round_to_dtype(x, dtype), dtype) for x in (q, k, v)]
+    return DecodeInputs(B, Hq, Hkv, Nq, Nk, d, dtype, bool(causal),
+                        default_scale(d) if scale is None else float(np.float32(scale)),
+                        int(seed), out[0], out[1], out[2], recipe)
+
+
+# Decoding workloads: one new token per sequence against a long cache, grouped-query
+# heads 32/8 (the pages' GQA example), batch 8.
+DECODE_WORKLOADS = {
+    "bf16_decode_b8_hq32_hkv8_nk8192_d128": dict(seed=1009, B=8, Hq=32, Hkv=8, Nq=1, Nk=8192,
+                                                 d=128, dtype="bf16", causal=True),
+    "bf16_decode_b1_hq32_hkv8_nk32768_d128": dict(seed=1010, B=1, Hq=32, Hkv=8, Nq=1, Nk=32768,
+                                                  d=128, dtype="bf16", causal=True),
+}
+
+
+def workload(name: str):
     """Generate one of the named workloads (may take seconds for the large ones)."""
+    if name in DECODE_WORKLOADS:
+        return make_decode_inputs(recipe=name, **DECODE_WORKLOADS[name])
     w = dict(WORKLOADS[name])
     w.pop("tuning", None)
     return make_inputs(recipe=name, **w)

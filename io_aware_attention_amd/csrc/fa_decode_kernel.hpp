@@ -238,4 +238,63 @@ fa_decode_kernel(DecodeArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the key-range pieces for few query rows (decoding has B*Hq*Nq of them,
+// often a few hundred): one workgroup per row, its threads spread over groups of
+// pieces as well as over columns, so that the pieces of a row are read in parallel
+// rather than one after another.  Same rule as fa_fwd_merge_kernel:
+// lse = log sum_s e^{lse_s},  O = sum_s e^{lse_s - lse} O_s.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) fa_decode_merge_kernel(FwdArgs a)
+{
+    constexpr int TPR = D / 4;                 // threads per piece: four columns each
+    constexpr int NG = 256 / TPR;              // groups of pieces
+    __shared__ float red_m[NG], red_w[NG];
+    __shared__ f32x4_t red_o[256];
+    const int64_t rows = (int64_t)a.B * a.Hq * a.N;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int col = (tid % TPR) * 4, grp = tid / TPR;
+
+    float m = -__builtin_inff();
+    for (int s = grp; s < a.num_splits; s += NG)
+        m = fmaxf(m, a.lse_part[s * rows + row]);
+    if (col == 0)
+        red_m[grp] = m;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        m = fmaxf(m, red_m[g]);
+
+    float w = 0.0f;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = grp; s < a.num_splits; s += NG) {
+        const float ls = a.lse_part[s * rows + row];
+        if (ls == -__builtin_inff())
+            continue;
+        const float e = __builtin_amdgcn_exp2f((ls - m) * 1.44269504088896341f);
+        acc += e * *reinterpret_cast<const f32x4_t *>(a.o_part + (s * rows + row) * D + col);
+        w += e;
+    }
+    red_o[tid] = acc;
+    if (col == 0)
+        red_w[grp] = w;
+    __syncthreads();
+    if (grp == 0) {
+        float wsum = 0.0f;
+        f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            o += red_o[g * TPR + tid];
+            wsum += red_w[g];
+        }
+        const float inv = 1.0f / wsum;
+        const u32x2_t y = {Mfma<T>::pack(o[0] * inv, o[1] * inv), Mfma<T>::pack(o[2] * inv, o[3] * inv)};
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.o) + row * D + col) = y;
+        if (col == 0 && a.lse)
+            a.lse[row] = m + kLn2 * __log2f(wsum);
+    }
+}
+
 }  // namespace fa355

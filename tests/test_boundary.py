@@ -220,3 +220,11 @@ def test_decode_rejections(kw, code):
 def test_decode_allows_more_queries_than_keys_without_causal_mask():
     # Nq > Nk is only an error under the causal mask (checked before any HIP call).
     assert decode_call(Nq=2, Nk=1, S=0, causal=0) == -5
+
+
+def test_decode_split_count_heuristic():
+    assert F.decode_split_count(8, 8, 8192) == 16          # 512 keys per piece
+    assert F.decode_split_count(1, 8, 32768) == 64
+    assert F.decode_split_count(1, 8, 4096) == 32          # one workgroup per CU
+    assert F.decode_split_count(1, 1, 100) == 1            # at least four blocks a piece
+    assert F.decode_split_count(1, 1, 1 << 22) == 256
