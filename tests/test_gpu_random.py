@@ -122,3 +122,25 @@ def test_random_backward(seed):
     TB.check(f"dq {_tag(c)}", dq, rq, bq)
     TB.check(f"dk {_tag(c)}", dk, rk, bk)
     TB.check(f"dv {_tag(c)}", dv, rv, bv)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode(seed):
+    import test_gpu_decode as TD
+    r = np.random.default_rng(36000 + seed)
+    Hkv = int(r.choice([1, 2, 4]))
+    G_ = int(r.choice([1, 2, 4, 8]))
+    Nq = int(r.integers(1, 32 // G_ + 1))
+    Nk = int(r.integers(Nq, 1500))
+    d = int(r.choice([64, 128]))
+    dt = str(r.choice(["bf16", "f16"]))
+    causal = bool(r.integers(0, 2))
+    S = int(r.integers(1, 40))
+    scale = float(r.choice([-1.0, 1.0])) * float(r.uniform(0.3, 1.5)) / np.sqrt(d)
+    B = int(r.choice([1, 2, 3]))
+    st = TD.draw(36000 + seed, B, Hkv * G_, Hkv, Nq, Nk, d, dt, float(r.choice([1.0, 2.0])))
+    q, k, v = (G.storage_to_f64(a, dt) for a in st)
+    o_ref, l_ref = oracle.attention_kv(q, k, v, causal, scale)
+    o, l = TD.run(st, dt, causal, scale, S)
+    PT.compare(o, l, o_ref, l_ref, dt, False,
+               f"{dt} B{B} H{Hkv * G_}x{Hkv} Nq{Nq} Nk{Nk} d{d} causal={causal} S{S} s{scale:+.3f}")
