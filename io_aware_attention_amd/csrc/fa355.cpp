@@ -328,7 +328,9 @@ const BwdVariant kBwdVariants[] = {
     FA355_BWD_VARIANTS(FA355_BWD_ROW, F16)
 };
 
-constexpr int kBwdTile = 128;   // query rows per dQ workgroup, keys per dK/dV workgroup
+constexpr int kBwdTile = 128;   // keys per dK/dV workgroup; queries per small dQ workgroup
+constexpr int kBwdTileWide = 256;   // queries per dQ workgroup while those still fill the CUs
+constexpr int kBwdCus = 256;
 
 int run_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
             const float *lse, float *dq, float *dk, float *dv, float *delta,
@@ -390,8 +392,12 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     a.Hkv = Hkv;
     a.N = N;
     a.group = Hq / Hkv;
-    a.n_qtiles = (int)n_tiles;
-    a.total_tiles = (int)(B * Hq * n_tiles);
+    // 256-query dQ workgroups share each staged K/V block over twice the queries;
+    // take them while there are still at least as many workgroups as CUs.
+    const int64_t wide = (N + kBwdTileWide - 1) / kBwdTileWide;
+    a.dq_rows = (int64_t)B * Hq * wide >= kBwdCus ? kBwdTileWide : kBwdTile;
+    a.n_qtiles = (int)(a.dq_rows == kBwdTileWide ? wide : n_tiles);
+    a.total_tiles = (int)(B * Hq * a.n_qtiles);
     a.n_ktiles = (int)n_tiles;
     float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
     if (!(c >= 1.17549435e-38f))

@@ -53,7 +53,8 @@ struct BwdArgs {
     float *dq, *dk, *dv;
     int B, Hq, Hkv, N;
     int group;          // Hq / Hkv
-    int n_qtiles;       // ceil(N / 128): query tiles of the dQ kernel
+    int dq_rows;        // queries per dQ workgroup: 128 or 256
+    int n_qtiles;       // ceil(N / dq_rows): query tiles of the dQ kernel
     int total_tiles;    // B * Hq * n_qtiles
     int n_ktiles;       // ceil(N / 128): key tiles of the dK/dV kernel
     float c;            // |scale| * log2(e), FLT_MIN for a zero scale

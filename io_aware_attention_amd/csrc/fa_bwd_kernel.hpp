@@ -19,9 +19,11 @@
 //                        dV accumulators in registers and walks every query block
 //                        of every query head sharing the K/V head (GQA), so dK and
 //                        dV need no atomics;
-//   fa_bwd_dq_kernel     one workgroup per (batch, query head, 128 queries): each
-//                        wavefront keeps 32 queries' Q and dO fragments and dQ,
-//                        and walks the key blocks.
+//   fa_bwd_dq_kernel     one workgroup per (batch, query head, 256 or 128 queries):
+//                        each wavefront keeps 32 queries' Q and dO fragments and
+//                        dQ, and walks the key blocks; the wider workgroup shares
+//                        each staged K/V block over more queries and is taken
+//                        while it still gives every CU a workgroup.
 // Matrix products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation;
 // P and dS are rounded to the input type only as matrix operands.  Gradients are
 // written in fp32.
@@ -301,11 +303,12 @@ fa_bwd_dkdv_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Workgroup: (batch, query head, 128 queries); wavefront: 32 queries.
+// dQ.  Workgroup: (batch, query head, 32 * WAVES queries); wavefront: 32 queries.
+// Half the wavefronts stage K, the other half V, for every key block.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int WAVES_>
 struct DqTraits {
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = WAVES_;
     static constexpr int BR = 32 * WAVES;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
@@ -316,11 +319,11 @@ struct DqTraits {
     static constexpr int STAGE = KL::BYTES + VL::BYTES;
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, bool CAUSAL, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 fa_bwd_dq_kernel(BwdArgs a)
 {
-    using Tr = DqTraits<T, D, CAUSAL>;
+    using Tr = DqTraits<T, D, CAUSAL, WAVES>;
     using M = Mfma<T>;
     using KL = typename Tr::KL;
     using VL = typename Tr::VL;
@@ -370,10 +373,11 @@ fa_bwd_dq_kernel(BwdArgs a)
     const int kv_len = CAUSAL ? min(N, i0 + Tr::BR) : N;
     const int n_kv = (kv_len + BC - 1) / BC;
     auto load_block = [&](int t, char *st) {
-        if (wave < 2)
-            dma_rows<D, 2>(kh, N, t * BC, st + Tr::K_OFF, wave, 2, lane);
+        constexpr int HALF = WAVES / 2;
+        if (wave < HALF)
+            dma_rows<D, 2>(kh, N, t * BC, st + Tr::K_OFF, wave, HALF, lane);
         else
-            dma_rows<D, 1>(vh, N, t * BC, st + Tr::V_OFF, wave - 2, 2, lane);
+            dma_rows<D, 1>(vh, N, t * BC, st + Tr::V_OFF, wave - HALF, HALF, lane);
     };
 
     load_block(0, stage0);

@@ -20,7 +20,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
                         dim3(a.B * a.Hkv * a.n_ktiles), dim3(256), params, 0, stream);
     if (e != hipSuccess)
         return e;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D, CAUSAL>),
+    if (a.dq_rows == 256)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D, CAUSAL, 8>),
+                               dim3(a.total_tiles), dim3(512), params, 0, stream);
+    if (a.dq_rows != 128)
+        return hipErrorInvalidValue;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D, CAUSAL, 4>),
                            dim3(a.total_tiles), dim3(256), params, 0, stream);
 }
 
