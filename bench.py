@@ -23,6 +23,11 @@ roofline    = the kernel's own rate: FLOPs per launch / average launch duration 
               size (read from profiles/, null when the kernel sources changed since).
 cpu_baseline = the fp64 CPU oracle, as it stands, on a bounded sample of query rows of
               the same workload, on this host's cores, in the same unit.
+Also reported, after the timed region: the median and minimum of per-launch HIP
+event times (roofline.kernel_us_median / kernel_us_min); the gfx clock read with
+amd-smi during sustained launches of the same kernel, with the peak scaled to that
+clock (clock); and, for HBM-bound lines, the same per-launch times with a 512 MB
+buffer read before each launch so that no input is left in L2 or the MALL (cold).
 """
 from __future__ import annotations
 
@@ -77,6 +82,113 @@ def load_traffic(workload: str):
     if not e or e.get("kernel_sha") != kernel_sha(srcs):
         return None
     return e.get("bytes_per_launch")
+
+
+def _amd_smi_gfx_mhz():
+    """Mean current gfx clock over the XCDs from `amd-smi metric -c --json`, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        clocks = d["gpu_data"][0]["clock"] if "gpu_data" in d else d[0]["clock"]
+        vals = [v["clk"]["value"] for k, v in clocks.items()
+                if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        return sum(vals) / len(vals) if vals else None
+    except Exception:  # noqa: BLE001 -- the tool is optional; no clock is reported then
+        return None
+
+
+def sustained_clock(step, sync, launch_us: float, samples: int = 2) -> dict | None:
+    """The gfx clock under this kernel's own sustained load.
+
+    After the timed region, keeps launching `step` (synchronising after about 20 ms
+    of queued launches) while a thread reads the clock `samples` times with
+    amd-smi; returns the mean reading, or None when amd-smi is unavailable.
+    """
+    import threading
+
+    got = []
+
+    def sampler():
+        time.sleep(0.3)
+        for _ in range(samples):
+            got.append(_amd_smi_gfx_mhz())
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    chunk = max(16, int(20000.0 / max(launch_us, 1.0)))
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < 60:
+        for _ in range(chunk):
+            step()
+        sync()
+    th.join()
+    vals = [g for g in got if g]
+    if not vals:
+        return None
+    return {"sclk_mhz": round(sum(vals) / len(vals), 1), "samples": len(vals),
+            "source": "amd-smi metric -c (mean of the XCDs' current gfx clock), read during "
+                      "sustained launches of the same kernel after the timed region"}
+
+
+def per_launch_us(step, stream, reps: int, flush=None):
+    """Median and minimum of `reps` launches, each bracketed by its own HIP events on
+    the launch stream; `flush` (if given) runs before each launch, outside the events."""
+    import torch
+
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    times.sort()
+    return times[len(times) // 2], times[0]
+
+
+def cache_flusher(dev, nbytes: int = 512 << 20):
+    """Reads a 512 MB scratch buffer (twice the 256 MB MALL) on the current stream.
+
+    A read rather than a write: written lines would still be dirty in L2 and the
+    MALL when the kernel starts, and their write-back would be charged to it."""
+    import torch
+
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    return lambda: torch.sum(buf, dim=0, out=out)
+
+
+def add_protocol_fields(line, step, stream, dev, reps, work, unit_scale, peak, cold):
+    """Per-launch median / minimum, the sustained clock, and (for HBM-bound lines) a
+    cold-cache variant, added beside the contract's fields.  `work` is the
+    algorithmic FLOPs or bytes of one launch, `unit_scale` turns work/us into the
+    roofline unit."""
+    import torch
+
+    med, mn = per_launch_us(step, stream, reps)
+    r = line["roofline"]
+    r["kernel_us_median"] = round(med, 2)
+    r["kernel_us_min"] = round(mn, 2)
+    r["achieved_median"] = round(work / med * unit_scale, 2)
+    if cold:
+        fl = cache_flusher(dev)
+        cmed, cmn = per_launch_us(step, stream, reps, flush=fl)
+        line["cold"] = {"kernel_us_median": round(cmed, 2), "kernel_us_min": round(cmn, 2),
+                        "achieved_median": round(work / cmed * unit_scale, 2), "unit": r["unit"],
+                        "frac": round(work / cmed * unit_scale / peak, 4),
+                        "how": "a 512 MB buffer read (summed) before each launch, outside its events"}
+    clk = sustained_clock(step, lambda: torch.cuda.synchronize(dev), r["kernel_us"])
+    if clk is not None and r["bound"] != "hbm":
+        # Matrix-core peak scales with the gfx clock (2400 MHz nominal); HBM's does not.
+        clk["peak_at_sclk"] = round(peak * clk["sclk_mhz"] / 2400.0, 1)
+        clk["frac_at_sclk"] = round(r["achieved"] / clk["peak_at_sclk"], 4)
+    line["clock"] = clk
 
 
 def device_inputs(x, dev):
@@ -265,6 +377,7 @@ def run_decode(args) -> dict:
                      "traffic": load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    add_protocol_fields(line, step, stream, dev, args.steps, nbytes, 1e-3, PEAK_HBM_GBS, cold=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_decode(x)
     return line
@@ -411,6 +524,8 @@ def run(args) -> dict:
     if args.bwd:
         line["config"]["pass"] = "backward (fa_bwd: delta, dK/dV, dQ kernels)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
+    add_protocol_fields(line, step, stream, dev, args.steps, nbytes if bound == "hbm" else flops,
+                        1e-3 if bound == "hbm" else 1e-6, peak, cold=bound == "hbm")
     if not args.no_cpu:
         line["cpu_baseline"] = (cpu_baseline_bwd(x, args.cpu_seconds) if args.bwd
                                 else cpu_baseline(x, args.cpu_seconds))
