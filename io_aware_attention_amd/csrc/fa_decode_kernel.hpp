@@ -240,59 +240,81 @@ fa_decode_kernel(DecodeArgs a)
 
 // ---------------------------------------------------------------------------
 // Merge of the key-range pieces for few query rows (decoding has B*Hq*Nq of them,
-// often a few hundred): one workgroup per row, its threads spread over groups of
-// pieces as well as over columns, so that the pieces of a row are read in parallel
-// rather than one after another.  Same rule as fa_fwd_merge_kernel:
+// from a few dozen up): one workgroup per (row, 32 columns).  Each thread takes one
+// piece's lse (there are at most 256 pieces), the workgroup forms the weights
+// e^{lse_s - max} in LDS, groups of 8 threads (four columns each) weight their
+// share of the pieces (loaded up front, with the lse values), and an LDS tree sums
+// the groups.  Same rule as fa_fwd_merge_kernel:
 // lse = log sum_s e^{lse_s},  O = sum_s e^{lse_s - lse} O_s.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256) fa_decode_merge_kernel(FwdArgs a)
 {
-    constexpr int TPR = D / 4;                 // threads per piece: four columns each
+    constexpr int CW = 32;                     // columns per workgroup
+    constexpr int TPR = CW / 4;                // threads per piece: four columns each
     constexpr int NG = 256 / TPR;              // groups of pieces
-    __shared__ float red_m[NG], red_w[NG];
-    __shared__ f32x4_t red_o[256];
+    __shared__ float wgt[256];
+    __shared__ float red_m[4], red_w[4];
+    __shared__ f32x4_t part[256];
     const int64_t rows = (int64_t)a.B * a.Hq * a.N;
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int col = (tid % TPR) * 4, grp = tid / TPR;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = a.num_splits;
+    constexpr int PER = 256 / NG;              // pieces per thread at most (S <= 256)
 
-    float m = -__builtin_inff();
-    for (int s = grp; s < a.num_splits; s += NG)
-        m = fmaxf(m, a.lse_part[s * rows + row]);
-    if (col == 0)
-        red_m[grp] = m;
-    __syncthreads();
+    // This thread's partials are loaded together with the lse values, so the
+    // merge waits on one round of memory reads, not two.
+    const int col = blockIdx.y * CW + (tid % TPR) * 4, grp = tid / TPR;
+    f32x4_t ov[PER];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-        m = fmaxf(m, red_m[g]);
-
-    float w = 0.0f;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = grp; s < a.num_splits; s += NG) {
-        const float ls = a.lse_part[s * rows + row];
-        if (ls == -__builtin_inff())
-            continue;
-        const float e = __builtin_amdgcn_exp2f((ls - m) * 1.44269504088896341f);
-        acc += e * *reinterpret_cast<const f32x4_t *>(a.o_part + (s * rows + row) * D + col);
-        w += e;
+    for (int i = 0; i < PER; ++i) {
+        const int s = grp + i * NG;
+        ov[i] = s < S ? *reinterpret_cast<const f32x4_t *>(a.o_part + ((int64_t)s * rows + row) * D + col)
+                      : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    red_o[tid] = acc;
-    if (col == 0)
-        red_w[grp] = w;
-    __syncthreads();
-    if (grp == 0) {
-        float wsum = 0.0f;
-        f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+    // The largest piece lse of the row.
+    const float ls = tid < S ? a.lse_part[tid * rows + row] : -__builtin_inff();
+    float m = ls;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            o += red_o[g * TPR + tid];
-            wsum += red_w[g];
-        }
+    for (int o = 32; o > 0; o >>= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0)
+        red_m[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    // A piece that saw no key has lse -inf and a zero partial: weight 0.
+    const float e = ls == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((ls - m) * 1.44269504088896341f);
+    wgt[tid] = e;
+    float w = e;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        w += __shfl_xor(w, o);
+    if (lane == 0)
+        red_w[wave] = w;
+    __syncthreads();
+
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int s = grp + i * NG;
+        if (s < S)
+            acc += wgt[s] * ov[i];
+    }
+    part[tid] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int st = NG / 2; st > 0; st >>= 1) {
+        if (grp < st)
+            part[tid] += part[tid + st * TPR];
+        __syncthreads();
+    }
+    if (tid < TPR) {
+        const float wsum = (red_w[0] + red_w[1]) + (red_w[2] + red_w[3]);
         const float inv = 1.0f / wsum;
+        const f32x4_t o = part[tid];
         const u32x2_t y = {Mfma<T>::pack(o[0] * inv, o[1] * inv), Mfma<T>::pack(o[2] * inv, o[3] * inv)};
         *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.o) + row * D + col) = y;
-        if (col == 0 && a.lse)
+        if (blockIdx.y == 0 && tid == 0 && a.lse)
             a.lse[row] = m + kLn2 * __log2f(wsum);
     }
 }

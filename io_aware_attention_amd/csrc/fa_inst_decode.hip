@@ -15,7 +15,7 @@ hipError_t launch_decode(const DecodeArgs &a, const FwdArgs &merge, hipStream_t 
     void *mparams[] = {&m};
     const int64_t rows = (int64_t)m.B * m.Hq * m.N;
     return hipLaunchKernel(reinterpret_cast<const void *>(&fa_decode_merge_kernel<T, D>),
-                           dim3((unsigned)rows), dim3(256), mparams, 0, stream);
+                           dim3((unsigned)rows, D / 32), dim3(256), mparams, 0, stream);
 }
 #define FA355_INST_DECODE(T, D, C) \
     template hipError_t launch_decode<T, D, C>(const DecodeArgs &, const FwdArgs &, hipStream_t);
