@@ -61,6 +61,9 @@ template <> struct Mfma<BF16> {
     // bf16 rounds P by up to 2^-8 relative, too coarse for a 1e-3 logsumexp: the
     // lse keeps its own fp32 sum of the unrounded P.
     static constexpr bool kSeparateLseSum = true;
+    // ... and too coarse to normalise O by that sum: O is divided by the sum of the
+    // rounded weights the P.V product used.
+    static constexpr bool kRoundedRowSum = true;
     // Largest lane sum of weights accepted without a rescale: bounds every weight,
     // hence O's accumulator at N 2^16 max|V|.
     static constexpr float kSumCap = 65536.0f;
@@ -81,6 +84,10 @@ template <> struct Mfma<BF16> {
 };
 template <> struct Mfma<F16> {
     static constexpr bool kSeparateLseSum = false;   // fp16 rounds P by <= 2^-11
+    // Rounding moves the row sum by at most 2^-11 relative: the fp32 sum of the
+    // unrounded weights normalises O as well (and spares the packed-pair dot
+    // products, which wait for the matrix pipe while an MFMA runs).
+    static constexpr bool kRoundedRowSum = false;
     // Weights are rounded to fp16 (largest finite 65504): a lane sum of rounded
     // weights at most 2^15 keeps each below that (an overflow to inf fails the test).
     static constexpr float kSumCap = 32768.0f;
@@ -201,8 +208,10 @@ struct FwdTraits {
     static constexpr int LDS = 2 * STAGE;
     static_assert(LDS == fwd_lds_bytes(D, BC), "LDS size");
     // Waves per SIMD to fit: two lets one wavefront's softmax run under the other's
-    // matrix work; head dim 256 needs the whole register file for one.
-    static constexpr int OCC = (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;
+    // matrix work; head dim 256 needs the whole register file for one.  At head dim
+    // 64 the fp16 kernel (one row sum) fits four in the register file.
+    static constexpr int OCC = (D <= 64 && WAVES == 4 && !Mfma<T>::kRoundedRowSum) ? 4
+                             : (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;
     static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
     static_assert(BR * (BC / 8) % (64 * WAVES) == 0, "bias tile DMA: whole instructions per wave");
 };
@@ -215,7 +224,9 @@ struct FwdTraits {
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool OUT_F32, bool SPLIT = false,
           bool BIAS = false>
 __global__ void __launch_bounds__(64 * WAVES)
-__attribute__((amdgpu_waves_per_eu(FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC)))
+// The split and bias variants hold more per lane: at most two wavefronts per SIMD.
+__attribute__((amdgpu_waves_per_eu((SPLIT || BIAS) && FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC > 2
+                                       ? 2 : FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>::OCC)))
 fa_fwd_kernel(FwdArgs a)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
@@ -440,8 +451,7 @@ fa_fwd_kernel(FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[jb][r], c, -m_sub));
-                        if constexpr (M::kSeparateLseSum)
-                            leb += p[r];
+                        leb += p[r];
                     }
                     // The row sum adds the rounded weights the P.V product uses, so O
                     // is an exact weighted mean of V rows with those weights.
@@ -451,7 +461,8 @@ fa_fwd_kernel(FwdArgs a)
                         for (int e = 0; e < 4; ++e) {
                             const uint32_t pk = M::pack(p[8 * s + 2 * e], p[8 * s + 2 * e + 1]);
                             pf[2 * jb + s][e] = pk;
-                            lb = M::sum2(pk, lb);
+                            if constexpr (M::kRoundedRowSum)
+                                lb = M::sum2(pk, lb);
                         }
                 }
             };
@@ -467,8 +478,7 @@ fa_fwd_kernel(FwdArgs a)
                                          : t != t_begin;
             if (fresh) {
                 weights(m_run);
-                const float sum = M::kSeparateLseSum ? leb : lb;
-                fresh = __builtin_amdgcn_ballot_w64(!(sum <= M::kSumCap)) == 0;
+                fresh = __builtin_amdgcn_ballot_w64(!(leb <= M::kSumCap)) == 0;
             }
             if (!fresh) {
                 float mx = sacc[0][0];
@@ -484,8 +494,7 @@ fa_fwd_kernel(FwdArgs a)
                 const float alpha = ((SPLIT || BIAS) && m_new == -__builtin_inff())
                                         ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_part *= alpha;
-                if constexpr (M::kSeparateLseSum)
-                    le_part *= alpha;
+                le_part *= alpha;
 #pragma unroll
                 for (int nb = 0; nb < Tr::NB; ++nb)
                     oacc[nb] *= alpha;
@@ -495,8 +504,7 @@ fa_fwd_kernel(FwdArgs a)
                 weights(((SPLIT || BIAS) && m_run == -__builtin_inff()) ? 0.0f : m_run);
             }
             l_part += lb;
-            if constexpr (M::kSeparateLseSum)
-                le_part += leb;
+            le_part += leb;
 
 #pragma unroll
             for (int nb = 0; nb < Tr::NB; ++nb) {
@@ -516,12 +524,12 @@ fa_fwd_kernel(FwdArgs a)
     }
 
     // Epilogue: O = O / l, lse = ln2 * (m + log2 l).
-    const f32x2_t lp = row_pair(l_part);
-    const float l_tot = lp[0] + lp[1];
-    float le_tot = l_tot;
-    if constexpr (M::kSeparateLseSum) {
-        const f32x2_t ep = row_pair(le_part);
-        le_tot = ep[0] + ep[1];
+    const f32x2_t ep = row_pair(le_part);
+    const float le_tot = ep[0] + ep[1];
+    float l_tot = le_tot;
+    if constexpr (M::kRoundedRowSum) {
+        const f32x2_t lp = row_pair(l_part);
+        l_tot = lp[0] + lp[1];
     }
     if (SPLIT && iq < N) {
         // Rows that saw no key in this split: weight zero in the merge.
