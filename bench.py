@@ -9,7 +9,9 @@
     python bench.py --decode [...]     # decoding against a key/value cache (fa_fwd_decode)
 
 A step is one pass of the whole hot path -- one fused forward kernel -- over one
-batch of seeded synthetic inputs already resident in device memory.  The default
+batch of seeded synthetic inputs already resident in device memory.  Before the W
+warm-up steps, the step is launched back to back for 0.25 s (settle): out of idle
+the clock takes ~20 ms to ramp, and steps timed inside the ramp run 10-30 % slow.  The default
 workload is the causal bf16 layer B=1, H=32, N=4096, d=128.  Prints one JSON line.
 
 value       = algorithmic FLOPs (4*B*Hq*N^2*d, halved when causal) * K / wall time of
@@ -23,11 +25,14 @@ roofline    = the kernel's own rate: FLOPs per launch / average launch duration 
               size (read from profiles/, null when the kernel sources changed since).
 cpu_baseline = the fp64 CPU oracle, as it stands, on a bounded sample of query rows of
               the same workload, on this host's cores, in the same unit.
-Also reported, after the timed region: the median and minimum of per-launch HIP
-event times (roofline.kernel_us_median / kernel_us_min); the gfx clock read with
-amd-smi during sustained launches of the same kernel, with the peak scaled to that
-clock (clock); and, for HBM-bound lines, the same per-launch times with a 512 MB
-buffer read before each launch so that no input is left in L2 or the MALL (cold).
+Also reported, after the timed region: the median and minimum of the time per
+launch over chunks of 10 back-to-back launches, each chunk bracketed by HIP events
+(roofline.kernel_us_median / kernel_us_min); the shader clock, measured by timing
+a spin kernel of known cycle counts between the kernel's launches, with the
+matrix-core peak scaled to it, beside amd-smi's readings (clock); and, for
+HBM-bound lines, the same with a 512 MB buffer read before each
+launch so that no input is left in L2 or the MALL, the reads timed alone and
+subtracted (cold).
 """
 from __future__ import annotations
 
@@ -84,6 +89,24 @@ def load_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+SETTLE_S = 0.25   # untimed launches before the warm-up steps: the clock ramps for ~20 ms
+
+
+def settle(step, sync, seconds: float = SETTLE_S) -> int:
+    """Launches `step` back to back for `seconds` of wall time (synchronising every
+    16 launches), so that the timed steps see the clock the kernel sustains rather
+    than the ramp out of idle: on an idle MI355X the first ~20 ms of launches of the
+    headline kernel run 10-30 % slower than the steady state.  Returns the count."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step()
+        n += 16
+        sync()
+    return n
+
+
 def _amd_smi_gfx_mhz():
     """Mean current gfx clock over the XCDs from `amd-smi metric -c --json`, or None."""
     import subprocess
@@ -124,32 +147,87 @@ def sustained_clock(step, sync, launch_us: float, samples: int = 2) -> dict | No
             step()
         sync()
     th.join()
-    vals = [g for g in got if g]
+    vals = sorted(g for g in got if g)
     if not vals:
         return None
-    return {"sclk_mhz": round(sum(vals) / len(vals), 1), "samples": len(vals),
-            "source": "amd-smi metric -c (mean of the XCDs' current gfx clock), read during "
-                      "sustained launches of the same kernel after the timed region"}
+    return {"sclk_mhz": round(vals[len(vals) // 2], 1), "samples_mhz": [round(v, 1) for v in vals],
+            "source": "amd-smi metric -c (mean of the XCDs' current gfx clock; median of the "
+                      "readings), read during sustained launches of the same kernel after the "
+                      "timed region"}
+
+
+CHUNK = 10   # launches per timed chunk for the median / minimum
+
+
+def _chunk_us(stream, chunks: int, body):
+    """Per-chunk times (us) of `chunks` runs of `body`, each bracketed by HIP events on
+    the launch stream, enqueued back to back and read after one synchronisation."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(chunks)]
+    for a, b in ev:
+        a.record(stream)
+        body()
+        b.record(stream)
+    stream.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def probe_clock_mhz(step, stream, rounds: int = 5) -> float:
+    """The shader clock while the kernel runs: torch's spin kernel waits a given
+    number of shader-clock cycles (the s_memtime counter); timed between launches of
+    `step` at two lengths, the slope cycles / time is the clock, free of the fixed
+    cost an event pair adds.  Median over `rounds`."""
+    import torch
+
+    short, long_ = 200_000, 2_200_000
+    est = []
+    for _ in range(rounds):
+        t = []
+        for cyc in (short, long_):
+            for _ in range(4):
+                step()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            torch.cuda._sleep(cyc)
+            b.record(stream)
+            for _ in range(4):
+                step()
+            stream.synchronize()
+            t.append(a.elapsed_time(b) * 1e3)
+        est.append((long_ - short) / (t[1] - t[0]))
+    est.sort()
+    return round(est[len(est) // 2], 1)
 
 
 def per_launch_us(step, stream, reps: int, flush=None):
-    """Median and minimum of `reps` launches, each bracketed by its own HIP events on
-    the launch stream; `flush` (if given) runs before each launch, outside the events."""
-    import torch
+    """Median and minimum over chunks of CHUNK back-to-back launches of the time per
+    launch (an event pair around a single launch adds ~25 us here).  With `flush`,
+    each launch is preceded by it, and the same chunks of flushes alone, timed
+    alternately, are subtracted."""
+    chunks = max(5, reps // CHUNK)
 
-    times = []
-    for _ in range(reps):
-        if flush is not None:
-            flush()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step()
-        b.record(stream)
-        b.synchronize()
-        times.append(a.elapsed_time(b) * 1e3)
-    times.sort()
-    return times[len(times) // 2], times[0]
+    def launches():
+        for _ in range(CHUNK):
+            if flush is not None:
+                flush()
+            step()
+
+    if flush is None:
+        per = sorted(t / CHUNK for t in _chunk_us(stream, chunks, launches))
+    else:
+        def flushes():
+            for _ in range(CHUNK):
+                flush()
+        per = []
+        for _ in range(chunks):
+            both = _chunk_us(stream, 1, launches)[0]
+            alone = _chunk_us(stream, 1, flushes)[0]
+            per.append((both - alone) / CHUNK)
+        per.sort()
+    return per[len(per) // 2], per[0]
 
 
 def cache_flusher(dev, nbytes: int = 512 << 20):
@@ -171,6 +249,8 @@ def add_protocol_fields(line, step, stream, dev, reps, work, unit_scale, peak, c
     roofline unit."""
     import torch
 
+    sync = lambda: torch.cuda.synchronize(dev)  # noqa: E731
+    settle(step, sync, 0.1)
     med, mn = per_launch_us(step, stream, reps)
     r = line["roofline"]
     r["kernel_us_median"] = round(med, 2)
@@ -182,9 +262,16 @@ def add_protocol_fields(line, step, stream, dev, reps, work, unit_scale, peak, c
         line["cold"] = {"kernel_us_median": round(cmed, 2), "kernel_us_min": round(cmn, 2),
                         "achieved_median": round(work / cmed * unit_scale, 2), "unit": r["unit"],
                         "frac": round(work / cmed * unit_scale / peak, 4),
-                        "how": "a 512 MB buffer read (summed) before each launch, outside its events"}
-    clk = sustained_clock(step, lambda: torch.cuda.synchronize(dev), r["kernel_us"])
-    if clk is not None and r["bound"] != "hbm":
+                        "how": "a 512 MB buffer read (summed) before each launch; chunks of "
+                               "10 (read, launch) pairs minus chunks of 10 reads alone"}
+    settle(step, sync, 0.1)
+    clk = {"sclk_mhz": probe_clock_mhz(step, stream),
+           "source": "shader-clock cycles of torch's spin kernel (two lengths, slope of their "
+                     "HIP-event times) enqueued between launches of the kernel, after settling"}
+    smi = sustained_clock(step, sync, r["kernel_us"])
+    if smi is not None:
+        clk["amd_smi"] = smi
+    if r["bound"] != "hbm":
         # Matrix-core peak scales with the gfx clock (2400 MHz nominal); HBM's does not.
         clk["peak_at_sclk"] = round(peak * clk["sclk_mhz"] / 2400.0, 1)
         clk["frac_at_sclk"] = round(r["achieved"] / clk["peak_at_sclk"], 4)
@@ -336,6 +423,7 @@ def run_decode(args) -> dict:
         torch.cuda.synchronize(dev)
         print(json.dumps({"profile_run": args.workload, "copy_bytes": src.numel() * 4}), flush=True)
         return {}
+    settled = settle(step, lambda: torch.cuda.synchronize(dev))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -377,6 +465,7 @@ def run_decode(args) -> dict:
                      "traffic": load_traffic(args.workload),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    line["settle"] = {"seconds": SETTLE_S, "launches": settled}
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes, 1e-3, PEAK_HBM_GBS, cold=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_decode(x)
@@ -457,6 +546,7 @@ def run(args) -> dict:
         print(json.dumps({"profile_run": args.workload, "copy_bytes": src.numel() * 4}), flush=True)
         return {}
 
+    settled = settle(step, lambda: torch.cuda.synchronize(dev))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -524,6 +614,7 @@ def run(args) -> dict:
     if args.bwd:
         line["config"]["pass"] = "backward (fa_bwd: delta, dK/dV, dQ kernels)"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
+    line["settle"] = {"seconds": SETTLE_S, "launches": settled}
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes if bound == "hbm" else flops,
                         1e-3 if bound == "hbm" else 1e-6, peak, cold=bound == "hbm")
     if not args.no_cpu:
