@@ -31,6 +31,10 @@
  * reached that point.  Calls are reentrant and thread-safe; the library keeps no
  * mutable state.  Errors: arguments are validated before any HIP call; on any
  * error the call returns a negative fa355_status and leaves o and lse untouched.
+ * Empty calls: with no query rows (B = 0, or N = 0; Nq = 0 for fa_fwd_decode) every
+ * entry point returns FA355_OK at once, enqueues nothing and touches no buffer, so
+ * any pointer may be NULL; only the sizes are checked (none negative, Hq and Hkv
+ * >= 1 with Hq % Hkv == 0).
  * There is no silent fallback: an unsupported head dimension, dtype or tiling is an
  * error, never a slower path (contrast "FlashAttention…昇腾…" page 2, pitfall).
  */
@@ -52,7 +56,7 @@ typedef enum {
 typedef enum {
     FA355_OK = 0,
     FA355_ERR_NULL = -1,        /* q, k, v or o is NULL                                   */
-    FA355_ERR_SHAPE = -2,       /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow  */
+    FA355_ERR_SHAPE = -2,       /* B or N < 0, Hq or Hkv < 1, Hq % Hkv != 0, or too large */
     FA355_ERR_UNSUPPORTED = -3, /* head dim, dtype pair or tiling not built               */
     FA355_ERR_ALIGN = -4,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte      */
     FA355_ERR_ARG = -5,         /* non-finite scale; o or lse overlapping another buffer  */

@@ -47,6 +47,16 @@ const Variant kVariants[] = {
 
 int elem_bytes(int dt) { return dt == FA355_F32 ? 4 : 2; }
 
+// A call with no query rows (B = 0 or N = 0) has nothing to compute.  Returns
+// FA355_OK for it, FA355_ERR_SHAPE for sizes no call may have (negative, or head
+// counts that do not divide), and 1 for a call with work to do.
+int empty_call(int B, int Hq, int Hkv, int N)
+{
+    if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+    return (B == 0 || N == 0) ? FA355_OK : 1;
+}
+
 // The built-in tile (br, bc) for an input type, head dim and sequence length,
 // chosen by measurement on MI355X (interleaved timings on one device).  From 4096
 // tokens at head dim 128, 256 query rows share each 64-key block (the K/V loads and
@@ -579,6 +589,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            fa355_dtype dtype, hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, dtype, nullptr, stream);
 }
 
@@ -587,6 +599,8 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               fa355_dtype in_dtype, fa355_dtype o_dtype,
               const fa355_tuning *tuning, hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, in_dtype, o_dtype, tuning,
                stream);
 }
@@ -596,6 +610,11 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
                  float scale, fa355_dtype in_dtype, fa355_dtype o_dtype,
                  const fa355_tuning *tuning, fa355_plan *plan)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0) {
+        if (e == FA355_OK && plan)
+            *plan = fa355_plan{};                  // no launch
+        return e;
+    }
     Checked c;
     const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, in_dtype,
                             o_dtype, tuning, c);
@@ -609,7 +628,7 @@ const char *fa_status_str(int status)
     switch (status) {
     case FA355_OK: return "ok";
     case FA355_ERR_NULL: return "a required pointer is NULL";
-    case FA355_ERR_SHAPE: return "bad shape (sizes < 1, Hq % Hkv != 0, or too large)";
+    case FA355_ERR_SHAPE: return "bad shape (negative sizes, heads < 1, Hq % Hkv != 0, or too large)";
     case FA355_ERR_UNSUPPORTED: return "unsupported head dim, dtype pair or tiling";
     case FA355_ERR_ALIGN: return "misaligned pointer (16 bytes for tensors, 4 for lse)";
     case FA355_ERR_ARG: return "bad argument (non-finite scale or overlapping buffers)";
@@ -623,6 +642,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            fa355_dtype dtype, hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
                    dtype, stream);
 }
@@ -632,6 +653,8 @@ int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *ls
                  fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
                  hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run_split(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, num_splits,
                      o_part, lse_part, stream);
 }
@@ -641,6 +664,8 @@ int fa_fwd_bias(const void *q, const void *k, const void *v, void *o, float *lse
                 long long bias_stride_row, int B, int Hq, int Hkv, int N, int d, int causal,
                 float scale, fa355_dtype dtype, hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run_bias(q, k, v, o, lse, bias, bias_stride_b, bias_stride_h, bias_stride_row, B, Hq,
                     Hkv, N, d, causal, scale, dtype, stream);
 }
@@ -649,6 +674,8 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                float q_descale, float k_descale, float v_descale, hipStream_t stream)
 {
+    if (const int e = empty_call(B, Hq, Hkv, N); e <= 0)
+        return e;
     return run_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, q_descale, k_descale,
                    v_descale, stream);
 }
@@ -658,6 +685,10 @@ int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *l
                   fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
                   hipStream_t stream)
 {
+    if (Nk < 0)
+        return FA355_ERR_SHAPE;
+    if (const int e = empty_call(B, Hq, Hkv, Nq); e <= 0)
+        return e;
     return run_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
                       o_part, lse_part, stream);
 }

@@ -215,6 +215,8 @@ def split_count(B: int, Hq: int, N: int, causal: bool, cus: int = 256, d: int = 
     B1 H2 N16384 d128 causal this picks 4; 3 to 6 measured within 2 % of each other."""
     rows, per_cu = (256, 2) if d == 128 else (128, 4)
     tiles = B * Hq * ((N + rows - 1) // rows)
+    if tiles == 0:                      # an empty call: nothing to split
+        return 1
     want = -(-per_cu * cus // tiles)
     blocks = (N + 63) // 64
     return max(1, min(16, want, blocks // 4))
@@ -332,6 +334,8 @@ def decode_split_count(B: int, Hkv: int, Nk: int, cus: int = 256) -> int:
     pieces.  (Measured on MI355X: B8 Hkv8 Nk8192 best at 16 pieces, B1 Hkv8 Nk32768
     at 32-64; fewer keys per piece lose to the per-piece set-up and merge.)"""
     blocks = (Nk + 31) // 32
+    if B * Hkv == 0 or blocks == 0:     # an empty call or an empty cache: one piece
+        return 1
     want = max(-(-blocks // 16), -(-cus // (B * Hkv)))
     return max(1, min(256, want, blocks // 4))
 

@@ -70,7 +70,7 @@ def test_valid_call_plans_a_launch():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
-    (dict(B_=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(N=0), -2),
+    (dict(B_=-1), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Hq=-2, Hkv=-1), -2),
     (dict(Hq=3, Hkv=2), -2), (dict(N=-5), -2), (dict(N=1 << 30), -2),
     (dict(d=96), -3), (dict(d=32), -3), (dict(d=512), -3), (dict(dt=F.F32, d=128), -3),
     (dict(dt=7), -3), (dict(odt=F.F16), -3), (dict(dt=F.F32, d=64, odt=F.BF16), -3),
@@ -84,6 +84,37 @@ def test_valid_call_plans_a_launch():
 def test_rejections(kw, code):
     rc, _ = check(**kw)
     assert rc == code, (kw, rc)
+
+
+def test_empty_calls_return_ok_without_touching_anything():
+    # No query rows: every entry point returns FA355_OK before any HIP call, with
+    # NULL buffers; only the sizes are checked.
+    L = F.lib()
+    for B_, N in ((0, 100), (1, 0), (0, 0)):
+        assert L.fa_fwd(None, None, None, None, None, B_, 4, 2, N, 128, 1, 0.1, F.BF16, None) == 0
+        assert L.fa_fwd_ex(None, None, None, None, None, B_, 4, 2, N, 96, 1, 0.1, F.BF16, F.BF16,
+                           None, None) == 0
+        assert L.fa_bwd(None, None, None, None, None, None, None, None, None, None,
+                        B_, 4, 2, N, 128, 1, 0.1, F.BF16, None) == 0
+        assert L.fa_fwd_split(None, None, None, None, None, B_, 4, 2, N, 128, 1, 0.1, F.BF16, 0,
+                              None, None, None) == 0
+        assert L.fa_fwd_bias(None, None, None, None, None, None, 0, 0, 0, B_, 4, 2, N, 128, 1, 0.1,
+                             F.BF16, None) == 0
+        assert L.fa_fwd_fp8(None, None, None, None, None, B_, 4, 2, N, 128, 1, 0.1, 1.0, 1.0, 1.0,
+                            None) == 0
+        assert L.fa_fwd_decode(None, None, None, None, None, B_, 8, 2, N, 100, 128, 1, 0.1, F.BF16,
+                               0, None, None, None) == 0
+    # The plan of an empty call launches nothing.
+    rc, p = check(q=None, k=None, v=None, o=None, lse=None, B_=0)
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid, p.lds_bytes) == (0, 0, 0, 0, 0)
+    # Sizes are still checked.
+    assert check(q=None, B_=0, Hq=3, Hkv=2)[0] == -2
+    assert check(q=None, B_=0, Hkv=0)[0] == -2
+    assert check(q=None, N=0, B_=-1)[0] == -2
+    assert L.fa_fwd_decode(None, None, None, None, None, 1, 8, 2, 0, -1, 128, 1, 0.1, F.BF16,
+                           4, None, None, None) == -2
+    assert L.fa_fwd_decode(None, None, None, None, None, 1, 8, 2, 0, 0, 128, 1, 0.1, F.BF16,
+                           4, None, None, None) == 0
 
 
 def test_fwd_validates_before_any_hip_call():
@@ -120,7 +151,7 @@ def bwd_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, do=BAS
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(do=None), -1), (dict(lse=None), -1), (dict(delta=None), -1),
-    (dict(dq=None), -1), (dict(B_=0), -2), (dict(Hq=3, Hkv=2), -2), (dict(N=0), -2),
+    (dict(dq=None), -1), (dict(B_=-1), -2), (dict(Hq=3, Hkv=2), -2), (dict(N=-1), -2),
     (dict(d=256), -3), (dict(d=96), -3), (dict(dt=F.F32, d=64), -3), (dict(dt=9), -3),
     (dict(scale=float("nan")), -5), (dict(q=BASE + 8), -4), (dict(dk=BASE + 7 * SPAN + 4), -4),
     (dict(lse=BASE + 5 * SPAN + 2), -4), (dict(dq=BASE), -5), (dict(dv=BASE + 7 * SPAN + 64), -5),
@@ -140,7 +171,7 @@ def split_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=None), -1), (dict(lp=None), -1), (dict(q=None), -1), (dict(S=0), -5), (dict(S=17), -5),
-    (dict(d=256), -3), (dict(dt=F.F32, d=64), -3), (dict(N=0), -2), (dict(op=BASE + 5 * SPAN + 8), -4),
+    (dict(d=256), -3), (dict(dt=F.F32, d=64), -3), (dict(N=-1), -2), (dict(op=BASE + 5 * SPAN + 8), -4),
     (dict(lp=BASE + 6 * SPAN + 2), -4), (dict(op=BASE + 8192), -5), (dict(lp=BASE + 5 * SPAN + 64), -5),
 ])
 def test_split_rejections(kw, code):
@@ -172,8 +203,8 @@ def fp8_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BA
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(B_=0), -2),
-    (dict(Hq=3, Hkv=2), -2), (dict(N=0), -2), (dict(N=1 << 30), -2), (dict(d=256), -3),
+    (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(B_=-1), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(N=-1), -2), (dict(N=1 << 30), -2), (dict(d=256), -3),
     (dict(d=96), -3), (dict(scale=float("inf")), -5), (dict(dq=0.0), -5), (dict(dk=-1.0), -5),
     (dict(dv=float("nan")), -5), (dict(dq=float("inf")), -5), (dict(dq=1e30, dk=1e30), -5),
     (dict(q=BASE + 8), -4), (dict(o=BASE + 3 * SPAN + 2), -4), (dict(lse=BASE + 4 * SPAN + 1), -4),
@@ -206,7 +237,7 @@ def decode_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1), (dict(o=None), -1),
-    (dict(B_=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(Hq=3), -2),
+    (dict(B_=-1), -2), (dict(Nq=-1), -2), (dict(Nk=0), -2), (dict(Hq=3), -2),
     (dict(Nq=101), -2), (dict(Nk=1 << 30), -2),
     (dict(Nq=9), -3), (dict(Hq=64, Hkv=1, Nq=1), -3), (dict(d=256), -3), (dict(dt=F.F32, d=64), -3),
     (dict(S=0), -5), (dict(S=257), -5), (dict(scale=float("nan")), -5),

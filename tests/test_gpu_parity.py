@@ -246,6 +246,41 @@ def test_errors_reported():
     assert e.value.status == -5
 
 
+def test_empty_inputs():
+    # No query rows (B = 0 or N = 0): every entry point succeeds, enqueues nothing and
+    # returns empty results; a normal call right after is unaffected.
+    dev = "cuda"
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    for B_, N in ((0, 64), (2, 0)):
+        q = torch.zeros(B_, 4, N, 128, **bf)
+        k = torch.zeros(B_, 2, N, 128, **bf)
+        o, lse = F.fwd(q, k, k.clone(), causal=True)
+        assert o.shape == (B_, 4, N, 128) and lse.shape == (B_, 4, N)
+        dq, dk, dv = F.bwd(q, k, k.clone(), o, o.clone(), lse, causal=True)
+        assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == k.shape
+        o, lse = F.fwd_split(q, k, k.clone(), causal=True)
+        assert o.shape == q.shape and lse.shape == (B_, 4, N)
+        o, lse = F.fwd_bias(q, k, k.clone(), torch.zeros(1, 1, N, N, **bf), causal=True)
+        assert o.shape == q.shape
+        q8 = torch.zeros(B_, 4, N, 128, dtype=torch.uint8, device=dev)
+        k8 = torch.zeros(B_, 2, N, 128, dtype=torch.uint8, device=dev)
+        o, lse = F.fwd_fp8(q8, k8, k8.clone(), 1.0, 1.0, 1.0, causal=True)
+        assert o.shape == (B_, 4, N, 128) and o.dtype == torch.bfloat16
+    # Decoding with no new queries against a non-empty cache.
+    qd = torch.zeros(1, 8, 0, 128, **bf)
+    kd = torch.ones(1, 2, 300, 128, **bf)
+    o, lse = F.fwd_decode(qd, kd, kd.clone(), causal=True)
+    assert o.shape == (1, 8, 0, 128) and lse.shape == (1, 8, 0)
+    torch.cuda.synchronize()
+    x = G.make_inputs(9901, 1, 2, 1, 130, 128, "bf16", True)
+    o_ref, l_ref = full_oracle(x)
+    q, k, v = PT.to_device(x)
+    o, l = F.fwd(q, k, v, causal=True, scale=x.scale)
+    torch.cuda.synchronize()
+    PT.compare(o.float().cpu().double().numpy(), l.cpu().double().numpy(), o_ref, l_ref, "bf16",
+               False, "after empty calls")
+
+
 @pytest.mark.parametrize("tl", [None, (128, 32), (64, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_growing_row_maximum(dt, tl):
