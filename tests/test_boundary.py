@@ -117,6 +117,19 @@ def test_empty_calls_return_ok_without_touching_anything():
                            4, None, None, None) == 0
 
 
+def test_largest_sizes_accepted_and_one_more_rejected():
+    # One head of 16-bit K or V must fit 32-bit byte offsets with 64 KiB to spare.
+    n_max = (2**31 - 1 - 65536) // 256                # d = 128: 8,388,351 rows
+    assert check(B_=1, Hq=1, Hkv=1, N=n_max)[0] == 0
+    assert check(B_=1, Hq=1, Hkv=1, N=n_max + 1)[0] == -2
+    n64 = (2**31 - 1 - 65536) // 128
+    assert check(B_=1, Hq=1, Hkv=1, N=n64, d=64)[0] == 0
+    assert check(B_=1, Hq=1, Hkv=1, N=n64 + 1, d=64)[0] == -2
+    # Decoding reads one 32-key block past the cache's end: n_max - 32 keys is the
+    # largest cache (run on the GPU in test_gpu_maxsize.py); one more is rejected.
+    assert decode_call(Nk=n_max - 32 + 1, Nq=2) == -2
+
+
 def test_fwd_validates_before_any_hip_call():
     # Invalid arguments return their code from fa_fwd / fa_fwd_ex without a GPU.
     L = F.lib()
