@@ -24,7 +24,8 @@ roofline    = the kernel's own rate: FLOPs per launch / average launch duration 
               rocprofv3 FETCH_SIZE / WRITE_SIZE counters, calibrated on a copy of known
               size (read from profiles/, null when the kernel sources changed since).
 cpu_baseline = the fp64 CPU oracle, as it stands, on a bounded sample of query rows of
-              the same workload, on this host's cores, in the same unit.
+              the same workload, on this host's cores, in the same unit; its
+              `parity` compares the GPU's output on that sample with the oracle's.
 Also reported, after the timed region: the median and minimum of the time per
 launch over chunks of 10 back-to-back launches, each chunk bracketed by HIP events
 (roofline.kernel_us_median / kernel_us_min); the shader clock, measured by timing
@@ -288,12 +289,42 @@ def device_inputs(x, dev):
     return out
 
 
-def cpu_baseline(x, budget_s: float = 15.0) -> dict:
+def _half_ulp(x, dtype: str):
+    """Half the spacing of a 16-bit float format at each |x| (one RNE store)."""
+    import numpy as np
+    p, emin = {"bf16": (8, -126), "f16": (11, -14)}[dtype]
+    _, e = np.frexp(np.abs(x))
+    e = np.where(x == 0, emin, np.maximum(e.astype(np.int64) - 1, emin))
+    return np.ldexp(0.5, e - (p - 1))
+
+
+def parity_of(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype: str, fp8: bool = False) -> dict:
+    """Errors of the GPU's output on the oracle's sample: max |O - O_ref| and
+    |lse - lse_ref|, and the worst ratio to the tolerance (1e-5 for fp32 outputs,
+    2e-2 plus half an output ulp for 16-bit ones; lse 1e-3).  e4m3 inputs have no
+    fixed tolerance (their per-element bounds follow from the e4m3 rounding of the
+    weights, computed by the GPU tests): errors only."""
+    import numpy as np
+    err = np.abs(o_gpu - o_ref)
+    lerr = np.abs(lse_gpu - lse_ref)
+    out = {"max_abs_o": float(err.max()), "max_abs_lse": float(lerr.max())}
+    if fp8:
+        out["tolerance"] = "per-element bounds from the e4m3 rounding (GPU tests)"
+        return out
+    bound = 1e-5 if out_dtype == "f32" else 2e-2 + _half_ulp(o_ref, out_dtype)
+    out["worst_o_err_over_tolerance"] = float((err / bound).max())
+    out["within_tolerance"] = bool((err <= bound).all() and (lerr <= 1e-3).all())
+    return out
+
+
+def cpu_baseline(x, budget_s: float = 15.0, gpu=None) -> dict:
     """Time the oracle on a bounded sample of the workload and scale to TFLOP/s.
 
     The sample is whole query heads (b = 0, heads 0, 1, ...) when one head takes
     less than the budget, otherwise every k-th query row of head 0.  FLOPs are
-    counted as for the GPU: 4*d per visible (query, key) pair.
+    counted as for the GPU: 4*d per visible (query, key) pair.  With `gpu` = (o,
+    lse, output dtype) of the same workload, the GPU's rows of the sample are
+    compared with the oracle's (`parity`).
     """
     import numpy as np
 
@@ -326,20 +357,32 @@ def cpu_baseline(x, budget_s: float = 15.0) -> dict:
         n_heads = min(x.Hq, max(G, n_heads // G * G))
         q, k, v = f64("q", 0, n_heads), f64("k", 0, n_heads // G), f64("v", 0, n_heads // G)
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, x.causal, x.scale, threads=threads)
+        o_ref, l_ref = oracle.attention(q, k, v, x.causal, x.scale, threads=threads)
         dt = time.perf_counter() - t0
         flops = head_flops * n_heads
         sample = f"all {x.N} query rows of heads 0..{n_heads - 1} (batch 0) of {x.recipe}"
+        pick = (0, slice(0, n_heads))
     else:
         every = int(math.ceil(head_flops / (rate * budget_s)))
         rows = np.arange(0, x.N, every, dtype=np.int64)
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, x.causal, x.scale, rows=rows, threads=threads)
+        o_ref, l_ref = oracle.attention(q, k, v, x.causal, x.scale, rows=rows, threads=threads)
         dt = time.perf_counter() - t0
         flops = row_flops(rows)
         sample = f"every {every}th query row of head (0,0) of {x.recipe}"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads"}
+        pick = (0, slice(0, 1), rows)
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads"}
+    if gpu is not None:
+        o, lse, odt = gpu
+        import torch  # noqa: F401 -- the GPU tensors are torch's
+        ri = None if len(pick) == 2 else torch.from_numpy(pick[2]).to(o.device)
+        og, lg = o[pick[0], pick[1]], lse[pick[0], pick[1]]
+        if ri is not None:
+            og, lg = og.index_select(1, ri), lg.index_select(1, ri)
+        out["parity"] = parity_of(og.float().cpu().double().numpy(), lg.cpu().double().numpy(),
+                                  o_ref[0], l_ref[0], odt, fp8=x.dtype == "e4m3")
+    return out
 
 
 def cpu_baseline_bwd(x, budget_s: float) -> dict:
@@ -377,19 +420,25 @@ def decode_bytes(x) -> int:
             + 4 * x.B * x.Hq * x.Nq)
 
 
-def cpu_baseline_decode(x) -> dict:
+def cpu_baseline_decode(x, gpu=None) -> dict:
     """The fp64 oracle, as it stands, on the whole decode workload, in GB/s of the
-    same compulsory bytes."""
+    same compulsory bytes; with `gpu` = (o, lse), the GPU's result is compared with
+    it (`parity`)."""
     import oracle
     from fa_inputs import storage_to_f64
 
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     q, k, v = (storage_to_f64(getattr(x, n), x.dtype) for n in "qkv")
     t0 = time.perf_counter()
-    oracle.attention_kv(q, k, v, x.causal, x.scale, threads=threads)
+    o_ref, l_ref = oracle.attention_kv(q, k, v, x.causal, x.scale, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": decode_bytes(x) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {x.recipe} workload; {dt:.2f} s in fp64 on {threads} threads"}
+    out = {"value": decode_bytes(x) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole {x.recipe} workload; {dt:.2f} s in fp64 on {threads} threads"}
+    if gpu is not None:
+        o, lse = gpu
+        out["parity"] = parity_of(o.float().cpu().double().numpy(), lse.cpu().double().numpy(),
+                                  o_ref, l_ref, x.dtype)
+    return out
 
 
 def run_decode(args) -> dict:
@@ -468,7 +517,7 @@ def run_decode(args) -> dict:
     line["settle"] = {"seconds": SETTLE_S, "launches": settled}
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes, 1e-3, PEAK_HBM_GBS, cold=True)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline_decode(x)
+        line["cpu_baseline"] = cpu_baseline_decode(x, gpu=(o, lse))
     return line
 
 
@@ -618,8 +667,11 @@ def run(args) -> dict:
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes if bound == "hbm" else flops,
                         1e-3 if bound == "hbm" else 1e-6, peak, cold=bound == "hbm")
     if not args.no_cpu:
+        # The bias line times the same oracle without its bias: no parity there.
+        odt = "bf16" if fp8 else x.dtype
+        gpu = None if (args.bwd or args.bias is not None) else (o, lse, odt)
         line["cpu_baseline"] = (cpu_baseline_bwd(x, args.cpu_seconds) if args.bwd
-                                else cpu_baseline(x, args.cpu_seconds))
+                                else cpu_baseline(x, args.cpu_seconds, gpu=gpu))
     return line
 
 
