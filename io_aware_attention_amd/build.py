@@ -1,9 +1,13 @@
 """Build libfa355.so (gfx950) in-tree with hipcc.
 
-    python -m io_aware_attention_amd.build [--jobs N] [--verbose]
+    python -m io_aware_attention_amd.build [--jobs N] [--verbose] [--lds-poison]
 
 Each shard of kernel variants compiles to its own object in parallel; the host
-C-ABI file links with them into io_aware_attention_amd/libfa355.so.
+C-ABI file links with them into io_aware_attention_amd/libfa355.so.  With
+--lds-poison the same sources build, with FA355_LDS_POISON=1, into
+libfa355_lds_poison.so: a debug library whose kernels fill every LDS stage with
+NaN bytes before refilling it and do not overlap staging with compute (its output
+must equal the normal library's bit for bit).
 """
 from __future__ import annotations
 
@@ -20,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libfa355.so")
+LDS_POISON_LIB_PATH = os.path.join(PKG, "libfa355_lds_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -36,9 +41,9 @@ def sources() -> list[str]:
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, out_dir: str, defines: list[str]) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *defines, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     t0 = time.time()
@@ -54,32 +59,36 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, lds_poison: bool = False) -> str:
     """Compile every kernel shard and the host library; returns the .so path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    out_dir = os.path.join(BUILD_DIR, "lds_poison") if lds_poison else BUILD_DIR
+    lib_path = LDS_POISON_LIB_PATH if lds_poison else LIB_PATH
+    defines = ["-DFA355_LDS_POISON=1"] if lds_poison else []
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 1)
     t0 = time.time()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, out_dir, defines), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs,
            "-Wl,--no-undefined"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s", flush=True)
-    return LIB_PATH
+        print(f"built {lib_path} in {time.time() - t0:.1f}s", flush=True)
+    return lib_path
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--lds-poison", action="store_true")
     a = ap.parse_args(argv)
-    build(a.jobs, a.verbose)
+    build(a.jobs, a.verbose, a.lds_poison)
     return 0
 
 

@@ -224,15 +224,27 @@ fa_bwd_dkdv_kernel(BwdArgs a)
         }
     };
 
-    if (steps > 0)
+    if (steps > 0) {
+        if constexpr (kLdsPoison) {
+            lds_poison<256>(stage0, Tr::STAGE, tid);
+            __syncthreads();
+        }
         load_step(0, stage0);
+    }
     __syncthreads();
 
     auto step = [&](auto par, int u) {
         constexpr int P = decltype(par)::value;
         const char *st = P == 0 ? stage0 : stage1;
-        if (u + 1 < steps)
+        if (u + 1 < steps) {
+            if constexpr (kLdsPoison) {
+                lds_poison<256>(P == 0 ? stage1 : stage0, Tr::STAGE, tid);
+                __syncthreads();
+            }
             load_step(u + 1, P == 0 ? stage1 : stage0);
+            if constexpr (kLdsPoison)
+                __syncthreads();
+        }
         const int i0 = (qb0 + u % per_head) * 32;
         if (!CAUSAL || i0 + 31 >= j0w) {
             const char *qb = st + Tr::Q_OFF, *gb = st + Tr::G_OFF;
@@ -380,14 +392,25 @@ fa_bwd_dq_kernel(BwdArgs a)
             dma_rows<D, 1>(vh, N, t * BC, st + Tr::V_OFF, wave - HALF, HALF, lane);
     };
 
+    if constexpr (kLdsPoison) {
+        lds_poison<64 * WAVES>(stage0, Tr::STAGE, tid);
+        __syncthreads();
+    }
     load_block(0, stage0);
     __syncthreads();
 
     auto step = [&](auto par, int t) {
         constexpr int P = decltype(par)::value;
         const char *st = P == 0 ? stage0 : stage1;
-        if (t + 1 < n_kv)
+        if (t + 1 < n_kv) {
+            if constexpr (kLdsPoison) {
+                lds_poison<64 * WAVES>(P == 0 ? stage1 : stage0, Tr::STAGE, tid);
+                __syncthreads();
+            }
             load_block(t + 1, P == 0 ? stage1 : stage0);
+            if constexpr (kLdsPoison)
+                __syncthreads();
+        }
         const int j0 = t * BC;
         if (iw0 < N && (!CAUSAL || j0 <= iw0 + 31)) {
             const char *kb = st + Tr::K_OFF, *vb = st + Tr::V_OFF;

@@ -122,16 +122,23 @@ fa_decode_kernel(DecodeArgs a)
     u32x4_t kf[DK];
     if (t_begin < t_end) {
         load_k(t_begin, kf);
+        if constexpr (kLdsPoison)
+            lds_poison<64>(smem + (t_begin & 1) * STAGE, STAGE, lane);
         load_v(t_begin);
     }
     for (int t = t_begin; t < t_end; ++t) {
         const int j0 = t * BC;
         u32x4_t kn[DK];
         load_k(t + 1, kn);                                 // past t_end: unused
+        if constexpr (kLdsPoison)
+            lds_poison<64>(smem + ((t + 1) & 1) * STAGE, STAGE, lane);
         load_v(t + 1);
         // The wait counts on the loads above being the latest ones issued.
         __builtin_amdgcn_sched_barrier(0);
-        wait_previous();                                   // K(t) and V(t) have landed
+        if constexpr (kLdsPoison)
+            __builtin_amdgcn_s_waitcnt(0);                 // every load has landed
+        else
+            wait_previous();                               // K(t) and V(t) have landed
         __builtin_amdgcn_sched_barrier(0);
 
         f32x16_t s = f32x16_t{};

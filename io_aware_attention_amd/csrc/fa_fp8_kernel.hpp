@@ -201,14 +201,26 @@ fa_fwd_fp8_kernel(FwdArgs a)
     float l_part = 0.0f;                       // this lane's half of the row sum
     const float c = a.c;
 
-    if (n_kv > 0)
+    if (n_kv > 0) {
+        if constexpr (kLdsPoison) {
+            lds_poison<Tr::NT>(smem, Tr::STAGE, tid);
+            __syncthreads();
+        }
         dma_block(0, 0);
+    }
     __syncthreads();
 
     for (int t = 0; t < n_kv; ++t) {
         const int j0 = t * BC;
-        if (t + 1 < n_kv)
+        if (t + 1 < n_kv) {
+            if constexpr (kLdsPoison) {
+                lds_poison<Tr::NT>(smem + ((t + 1) & 1) * Tr::STAGE, Tr::STAGE, tid);
+                __syncthreads();
+            }
             dma_block(t + 1, (t + 1) & 1);
+            if constexpr (kLdsPoison)
+                __syncthreads();
+        }
 
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {

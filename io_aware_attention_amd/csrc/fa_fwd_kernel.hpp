@@ -126,6 +126,26 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, int v
 #endif
 }
 
+// Debug build (-DFA355_LDS_POISON=1): before each LDS stage is refilled, every byte
+// of it is set to 0xff -- a NaN as bf16, fp16, fp32 and e4m3 -- and each refill is
+// waited for before the block in the other stage is computed.  A read of LDS that
+// no copy wrote then turns into NaN, and staging cannot overlap compute, so the
+// output must match the normal build bit for bit.  The normal build compiles none
+// of it.
+#ifndef FA355_LDS_POISON
+#define FA355_LDS_POISON 0
+#endif
+constexpr bool kLdsPoison = FA355_LDS_POISON != 0;
+
+// Fills `bytes` (a multiple of 16) of LDS at `dst` with 0xff bytes, 16 per thread
+// per pass, from the NT threads of the workgroup, and waits for the stores.
+template <int NT>
+__device__ __forceinline__ void lds_poison(char *dst, int bytes, int tid) {
+    for (int off = tid * 16; off < bytes; off += NT * 16)
+        *reinterpret_cast<u32x4_t *>(dst + off) = u32x4_t{~0u, ~0u, ~0u, ~0u};
+    __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): the stores have landed
+}
+
 // ds_read_b64_tr_b16: each group of 16 lanes reads a 4-row x 16-column block of
 // 16-bit values (lane L addresses 8 bytes of row (L % 16) / 4); lane L receives
 // the four values of column L % 16, rows 0..3 in order.
@@ -358,14 +378,26 @@ fa_fwd_kernel(FwdArgs a)
     // soon as they leave the matrix cores, and the multiplier below becomes 1.
     const float c = BIAS ? 1.0f : a.c;
 
-    if (t_begin < n_kv)
+    if (t_begin < n_kv) {
+        if constexpr (kLdsPoison) {
+            lds_poison<Tr::NT>(smem, STAGE, tid);
+            __syncthreads();
+        }
         dma_block(t_begin, 0);
+    }
     __syncthreads();
 
     for (int t = t_begin; t < n_kv; ++t) {
         const int j0 = t * BC;
-        if (t + 1 < n_kv)
+        if (t + 1 < n_kv) {
+            if constexpr (kLdsPoison) {
+                lds_poison<Tr::NT>(smem + ((t + 1 - t_begin) & 1) * STAGE, STAGE, tid);
+                __syncthreads();
+            }
             dma_block(t + 1, (t + 1 - t_begin) & 1);
+            if constexpr (kLdsPoison)
+                __syncthreads();
+        }
 
         // Blocks wholly above this wavefront's causal diagonal, and wavefronts
         // wholly past N, have nothing to add.
@@ -672,6 +704,10 @@ fa_fwd_f32_kernel(FwdArgs a)
     for (int t = 0; t < n_kv; ++t) {
         const int j0 = t * BC;
         __syncthreads();
+        if constexpr (kLdsPoison) {
+            lds_poison<Tr::NT>(smem, Tr::LDS, tid);
+            __syncthreads();
+        }
         for (int x = tid; x < BC * D; x += Tr::NT) {
             const int row = x / D, col = x % D;
             const bool in = j0 + row < N;

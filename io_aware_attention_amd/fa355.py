@@ -9,12 +9,16 @@ fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa355.so")
+# The debug build of the same sources (LDS stages filled with NaN bytes before each
+# refill, no overlap of staging with compute): must give the same bits.
+LDS_POISON_LIB_PATH = os.path.join(HERE, "libfa355_lds_poison.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
@@ -42,15 +46,11 @@ class Plan(ctypes.Structure):
 _lib = None
 
 
-def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise FA355Error(ERR_HIP, f"{LIB_PATH} is not built; run "
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise FA355Error(ERR_HIP, f"{path} is not built; run "
                          "`python -m io_aware_attention_amd.build` first")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, ip, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     common = [vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, fp]
     L.fa_fwd.argtypes = common + [ip, vp]
@@ -74,8 +74,28 @@ def lib() -> ctypes.CDLL:
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
     L.fa_version.restype = ip
-    _lib = L
     return L
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Routes this module's calls to another build of the library (e.g. the LDS
+    poison debug build) inside the `with` block.  Not thread-safe."""
+    global _lib
+    prev = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
 
 
 def status_str(status: int) -> str:

@@ -25,9 +25,10 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == set(B.EXPORTS), names
-    L = ctypes.CDLL(B.LIB_PATH)
-    for n in names:
-        assert hasattr(L, n), n
+    for path in (B.LIB_PATH, B.LDS_POISON_LIB_PATH):
+        L = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(L, n), (path, n)
 
 
 def test_version_and_status_strings():
