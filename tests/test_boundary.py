@@ -273,3 +273,36 @@ def test_decode_split_count_heuristic():
     assert F.decode_split_count(1, 8, 4096) == 32          # one workgroup per CU
     assert F.decode_split_count(1, 1, 100) == 1            # at least four blocks a piece
     assert F.decode_split_count(1, 1, 1 << 22) == 256
+
+
+def test_library_imports_no_allocating_or_copying_call():
+    """The library allocates, clears and copies nothing (the forward pass keeps O(N)
+    state, never an N x N matrix): of the HIP runtime it imports only kernel
+    registration, the launch and the per-kernel LDS attribute."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not installed")
+    allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipFuncSetAttribute",
+               "hipLaunchKernel"}
+    for path in (B.LIB_PATH, B.LDS_POISON_LIB_PATH):
+        out = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        hip = {line.split()[-1].split("@")[0] for line in out.splitlines()
+               if "hip" in line.lower()}
+        assert hip and hip <= allowed, (path, sorted(hip - allowed))
+
+
+def test_use_library_restores_the_previous_library():
+    before = B.lib()
+    with pytest.raises(RuntimeError):
+        with B.use_library(B.LDS_POISON_LIB_PATH) as dbg:
+            assert B.lib() is dbg and dbg is not before
+            raise RuntimeError("leave the block")
+    assert B.lib() is before
+    with pytest.raises(B.FA355Error):
+        with B.use_library(B.LIB_PATH + ".missing"):
+            pass
+    assert B.lib() is before
