@@ -143,3 +143,21 @@ def test_quantize_e4m3_per_tensor_descale():
     cq, dq = G.quantize_e4m3(q)
     assert np.array_equal(a.q, cq) and a.descale[0] == dq
     assert np.array_equal(a.f64("q"), dq * G.storage_to_f64(cq, "e4m3"))
+
+
+def test_every_workload_matches_its_stored_hash():
+    """Each named workload's inputs are bit-identical to those the stored hashes were
+    taken from (tests/golden/make_input_hashes.py, which calls only this module)."""
+    import importlib.util
+    import json
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_input_hashes",
+                                                  os.path.join(here, "make_input_hashes.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    with open(os.path.join(here, "input_hashes.json")) as f:
+        stored = json.load(f)
+    assert set(stored) == set(G.WORKLOADS) | set(G.DECODE_WORKLOADS)
+    for name, want in stored.items():
+        assert mk.digest(G.workload(name)) == want, name
