@@ -35,6 +35,9 @@
  * entry point returns FA355_OK at once, enqueues nothing and touches no buffer, so
  * any pointer may be NULL; only the sizes are checked (none negative, Hq and Hkv
  * >= 1 with Hq % Hkv == 0).
+ * Size limits (FA355_ERR_SHAPE beyond them): every tensor a call touches holds at
+ * most 2^40 elements, and one head of each tensor fits the kernels' 32-bit byte
+ * offsets (N d elem_bytes <= 2^31 - 1 - 65536; each entry point states its own).
  * There is no silent fallback: an unsupported head dimension, dtype or tiling is an
  * error, never a slower path (contrast "FlashAttention…昇腾…" page 2, pitfall).
  */
@@ -133,7 +136,8 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
  *              dimension (e.g. one [N,N] bias for every batch and head).
  *   strides    in elements; bias_stride_row >= N; all strides multiples of 4 and
  *              bias 8-byte aligned (FA355_ERR_ALIGN); negative strides or a row
- *              stride below N are FA355_ERR_ARG
+ *              stride below N are FA355_ERR_ARG; a bias whose extent (last element
+ *              addressed, plus one) exceeds 2^40 elements is FA355_ERR_SHAPE
  *   dtype      F16 or BF16; d in {64, 128}; output in the input dtype
  * Otherwise as fa_fwd.  Reads the bias once per (query row, key) it needs:
  * B*Hq*N^2*2 bytes (halved when causal) on top of the forward's traffic.

@@ -80,6 +80,17 @@ void default_tile(int dt, int d, int N, int &br, int &bc)
     }
 }
 
+// The largest tensor any call accepts, in elements: 2^40 (4 TiB of fp32, far beyond
+// one device's memory).  Under it, byte extents -- up to 256 split partials of 4
+// bytes per element, 2^50 bytes -- and the overlap tests below cannot wrap.
+constexpr unsigned __int128 kMaxElems = (unsigned __int128)1 << 40;
+
+// True if a [B, H, N, d] tensor exceeds kMaxElems (sizes already checked >= 0).
+bool too_large(int B, int H, int N, int d)
+{
+    return (unsigned __int128)B * (unsigned)H * (unsigned)N * (unsigned)d > kMaxElems;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -99,6 +110,8 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
     if (!q || !k || !v || !o)
         return FA355_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+    if (too_large(B, Hq, N, d > 0 ? d : 0))
         return FA355_ERR_SHAPE;
 
     if (in_dt != FA355_F32 && in_dt != FA355_F16 && in_dt != FA355_BF16)
@@ -300,6 +313,13 @@ int run_bias(const void *q, const void *k, const void *v, void *o, float *lse,
     // Rows are read four keys (8 bytes) at a time.
     if (sb < 0 || sh < 0 || si < N)
         return FA355_ERR_ARG;
+    // The bias's extent in elements, in 128 bits (strides are the caller's 64-bit
+    // values): beyond the largest tensor any call accepts it is too large.
+    const unsigned __int128 extent = (unsigned __int128)(B - 1) * (unsigned long long)sb +
+                                     (unsigned __int128)(Hq - 1) * (unsigned long long)sh +
+                                     (unsigned __int128)(N - 1) * (unsigned long long)si + N;
+    if (extent > kMaxElems)
+        return FA355_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(bias) % 8 || si % 4 || sh % 4 || sb % 4)
         return FA355_ERR_ALIGN;
     // One (batch, head) slice of the bias is addressed with 32-bit byte offsets.
@@ -350,6 +370,8 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
         return FA355_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
+        return FA355_ERR_SHAPE;
+    if (too_large(B, Hq, N, d > 0 ? d : 0))
         return FA355_ERR_SHAPE;
     if ((dt != FA355_F16 && dt != FA355_BF16) || (d != 64 && d != 128))
         return FA355_ERR_UNSUPPORTED;
@@ -429,6 +451,8 @@ int run_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
         return FA355_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0)
         return FA355_ERR_SHAPE;
+    if (too_large(B, Hq, N, d > 0 ? d : 0))
+        return FA355_ERR_SHAPE;
     if (d != 64 && d != 128)
         return FA355_ERR_UNSUPPORTED;
     if ((int64_t)N * d * 2 > INT_MAX - 65536)       // one head of o, 32-bit offsets
@@ -497,6 +521,8 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
     if (!q || !k || !v || !o || !o_part || !lse_part)
         return FA355_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0 || (causal && Nq > Nk))
+        return FA355_ERR_SHAPE;
+    if (too_large(B, Hq, Nq, d > 0 ? d : 0) || too_large(B, Hkv, Nk, d > 0 ? d : 0))
         return FA355_ERR_SHAPE;
     if ((dt != FA355_F16 && dt != FA355_BF16) || (d != 64 && d != 128))
         return FA355_ERR_UNSUPPORTED;

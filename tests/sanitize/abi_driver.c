@@ -79,6 +79,35 @@ int main(void)
     EXPECT(fa_fwd_decode(P(1), P(2), P(3), P(4), F(5), 1, 8, 2, 2, 8388320, 128, 1, 0.1f, FA355_BF16, 4, F(6),
                          F(7), NULL), FA355_ERR_SHAPE);
 
+    /* Sizes whose byte extents would wrap a 64-bit count: too large, not an overlap,
+     * and no signed overflow on the way (UBSan checks the arithmetic). */
+    const int big = 1 << 30;
+    EXPECT(fa_fwd_check(P(1), P(2), P(3), P(4), F(5), big, big, big, 4096, 128, 1, 0.1f, FA355_BF16,
+                        FA355_BF16, NULL, &plan), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_check(P(1), P(2), P(3), P(4), F(5), 2147483647, 2147483647, 1, 8388351, 128, 0, 0.1f,
+                        FA355_BF16, FA355_F32, NULL, &plan), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_check(P(1), P(2), P(3), P(4), F(5), 2048, 4096, 4096, 8192, 128, 1, 0.1f, FA355_BF16,
+                        FA355_BF16, NULL, &plan), FA355_ERR_SHAPE);           /* 2^43 elements */
+    EXPECT(fa_fwd_check(P(1), P(2), P(3), P(4), F(5), 256, 4096, 4096, 8192, 128, 1, 0.1f, FA355_BF16,
+                        FA355_BF16, NULL, &plan), FA355_ERR_ARG);  /* 2^40: accepted size, 2 TiB overlap */
+    EXPECT(fa_fwd(P(1), P(2), P(3), P(4), F(5), big, 8, 8, 4096, 128, 1, 0.1f, FA355_F16, NULL),
+           FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_split(P(1), P(2), P(3), P(4), F(5), big, 8, 8, 4096, 128, 1, 0.1f, FA355_BF16, 4, F(6),
+                        F(7), NULL), FA355_ERR_SHAPE);
+    EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), F(6), F(7), F(8), F(9), F(10), big, big, 1, 4096, 128, 1,
+                  0.1f, FA355_BF16, NULL), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_fp8(P(1), P(2), P(3), P(4), F(5), big, big, 1, 4096, 128, 1, 0.1f, 1.0f, 1.0f, 1.0f,
+                      NULL), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_decode(P(1), P(2), P(3), P(4), F(5), big, 8, 8, 1, 8388000, 128, 1, 0.1f, FA355_BF16, 256,
+                         F(6), F(7), NULL), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_bias(P(1), P(2), P(3), P(4), F(5), P(6), 4611686018427387904LL, 0, 128, 2, 4, 2, 100, 128, 1,
+                       0.1f, FA355_BF16, NULL), FA355_ERR_SHAPE);
+    EXPECT(fa_fwd_bias(P(1), P(2), P(3), P(4), F(5), P(6), 9223372036854775804LL, 9223372036854775804LL, 128,
+                       1 << 10, 4, 2, 100, 128, 1, 0.1f, FA355_BF16, NULL), FA355_ERR_SHAPE);
+    /* Just under the limits: accepted by planning. */
+    EXPECT(fa_fwd_check(P(1), P(2), P(3), P(4), F(5), 64, 64, 8, 65536, 128, 1, 0.1f, FA355_BF16,
+                        FA355_BF16, NULL, &plan), FA355_OK);                  /* 2^35 elements */
+
     /* Empty calls: success, nothing touched, NULL pointers allowed. */
     EXPECT(fa_fwd(NULL, NULL, NULL, NULL, NULL, 0, 4, 2, 100, 128, 1, 0.1f, FA355_BF16, NULL), FA355_OK);
     EXPECT(fa_bwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 4, 2, 0, 128, 1, 0.1f,

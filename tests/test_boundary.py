@@ -131,6 +131,24 @@ def test_largest_sizes_accepted_and_one_more_rejected():
     assert decode_call(Nk=n_max - 32 + 1, Nq=2) == -2
 
 
+def test_tensors_above_2_40_elements_are_too_large():
+    # Byte extents of such tensors could wrap a 64-bit count; they are rejected as too
+    # large before any extent is computed (not misreported as an overlap).
+    far = 1 << 46                                     # fake tensors 64 TiB apart
+    kw = dict(q=BASE, k=BASE + far, v=BASE + 2 * far, o=BASE + 3 * far, lse=BASE + 4 * far)
+    assert check(**kw, B_=2048, Hq=4096, Hkv=4096, N=8192, d=128)[0] == -2      # 2^43
+    assert check(**kw, B_=2**30, Hq=2**30, Hkv=2**30, N=4096, d=128)[0] == -2
+    assert check(**kw, B_=256, Hq=4096, Hkv=4096, N=8192, d=128)[0] == 0       # exactly 2^40
+    assert check(B_=256, Hq=4096, Hkv=4096, N=8192, d=128)[0] == -5            # 4 GiB apart: overlap
+    L = F.lib()
+    assert L.fa_fwd_bias(BASE, BASE + SPAN, BASE + 2 * SPAN, BASE + 3 * SPAN, BASE + 4 * SPAN,
+                         BASE + 5 * SPAN, 2**62, 0, 128, 2, 4, 2, 100, 128, 1, 0.1, F.BF16, None) == -2
+    assert L.fa_fwd_bias(BASE, BASE + SPAN, BASE + 2 * SPAN, BASE + 3 * SPAN, BASE + 4 * SPAN,
+                         BASE + 5 * SPAN, 2**63 - 4, 2**63 - 4, 128, 1024, 4, 2, 100, 128, 1, 0.1,
+                         F.BF16, None) == -2
+    assert decode_call(B_=2**30, Hq=8, Hkv=8, Nq=1, Nk=8388000, S=256) == -2
+
+
 def test_fwd_validates_before_any_hip_call():
     # Invalid arguments return their code from fa_fwd / fa_fwd_ex without a GPU.
     L = F.lib()
