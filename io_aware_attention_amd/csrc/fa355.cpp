@@ -63,7 +63,7 @@ int empty_call(int B, int Hq, int Hkv, int N)
 // the per-block bookkeeping are spread over more rows: 140 us against 144 us for
 // 128 x 32 on the causal B1 H32 N4096 layer); shorter sequences keep 128-row tiles
 // with 32-key blocks, whose lower register use fits three wavefronts per SIMD.
-void default_tile(int dt, int d, int N, int &br, int &bc)
+void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
 {
     if (dt == FA355_F32) {
         br = 32;
@@ -74,7 +74,15 @@ void default_tile(int dt, int d, int N, int &br, int &bc)
     } else if (d == 128) {
         br = N >= 4096 ? 256 : 128;
         bc = N >= 4096 ? 64 : 32;
+    } else if (dt == FA355_BF16) {
+        // d = 64, bf16 (two wavefronts per SIMD for every tile; measured on MI355X,
+        // interleaved): 256 x 64 without a mask (4-8 % ahead from N = 512 up), and
+        // causal from N = 2048; 128 x 32 for shorter causal rows.
+        const bool wide = !causal || N >= 2048;
+        br = wide ? 256 : 128;
+        bc = wide ? 64 : 32;
     } else {
+        // d = 64, fp16: 128 x 64 runs four wavefronts per SIMD and is ahead or even.
         br = 128;
         bc = 64;
     }
@@ -143,7 +151,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
         return FA355_ERR_ARG;
 
     int br, bc;
-    default_tile(in_dt, d, N, br, bc);
+    default_tile(in_dt, d, N, causal != 0, br, bc);
     if (tuning && (tuning->br != 0 || tuning->bc != 0)) {
         br = tuning->br;
         bc = tuning->bc;

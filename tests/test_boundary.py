@@ -65,6 +65,11 @@ def test_valid_call_plans_a_launch():
     assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
     rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
     assert rc == 0 and (p.br, p.bc) == (128, 64)
+    # d = 64: fp16 keeps 128 x 64; bf16 takes 256 x 64, except causal rows below 2048.
+    assert check(d=64, N=512, dt=F.F16, causal=0)[1].br == 128
+    assert (check(d=64, N=512, causal=0)[1].br, check(d=64, N=512, causal=0)[1].bc) == (256, 64)
+    assert (check(d=64, N=2047, causal=1)[1].br, check(d=64, N=2047, causal=1)[1].bc) == (128, 32)
+    assert (check(d=64, N=2048, causal=1)[1].br, check(d=64, N=2048, causal=1)[1].bc) == (256, 64)
     rc, p = check(lse=None)
     assert rc == 0
 
