@@ -72,8 +72,11 @@ void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
         br = 128;
         bc = 64;
     } else if (d == 128) {
-        br = N >= 4096 ? 256 : 128;
-        bc = N >= 4096 ? 64 : 32;
+        // 256 x 64 from N = 4096 (causal) or N = 2048 (no mask), 128 x 32 below
+        // (measured on MI355X, interleaved: non-causal N = 2048 142 against 145 us).
+        const bool wide = N >= 4096 || (!causal && N >= 2048);
+        br = wide ? 256 : 128;
+        bc = wide ? 64 : 32;
     } else if (dt == FA355_BF16) {
         // d = 64, bf16 (two wavefronts per SIMD for every tile; measured on MI355X,
         // interleaved): 256 x 64 without a mask (4-8 % ahead from N = 512 up), and

@@ -70,6 +70,9 @@ def test_valid_call_plans_a_launch():
     assert (check(d=64, N=512, causal=0)[1].br, check(d=64, N=512, causal=0)[1].bc) == (256, 64)
     assert (check(d=64, N=2047, causal=1)[1].br, check(d=64, N=2047, causal=1)[1].bc) == (128, 32)
     assert (check(d=64, N=2048, causal=1)[1].br, check(d=64, N=2048, causal=1)[1].bc) == (256, 64)
+    # d = 128: 256 x 64 from N = 4096, or from N = 2048 without a mask.
+    assert check(N=2048, causal=1)[1].br == 128 and check(N=2048, causal=0)[1].br == 256
+    assert check(N=2047, causal=0)[1].br == 128 and check(N=4096, causal=1)[1].br == 256
     rc, p = check(lse=None)
     assert rc == 0
 
