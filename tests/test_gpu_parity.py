@@ -70,6 +70,24 @@ def test_small_full_parity(cfg):
         PT.compare(o32, l32, o_ref, l_ref, dt, True, _small_id(cfg) + " f32-out")
 
 
+# Either side of the sequence lengths where the default tile changes (bf16 at d = 64
+# causal: 128 x 32 below 2048, 256 x 64 from it; d = 128 without a mask: the same
+# switch at 2048; d = 128 causal: at 4096), each with a ragged last tile.
+SWITCH = [
+    (1, 2, 2, 2047, 64, "bf16", True), (1, 2, 2, 2048, 64, "bf16", True),
+    (1, 2, 1, 2047, 128, "bf16", False), (1, 2, 1, 2048, 128, "f16", False),
+    (1, 2, 2, 4095, 128, "bf16", True), (1, 2, 2, 4097, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dt,causal", SWITCH)
+def test_default_tile_switch_points(B, Hq, Hkv, N, d, dt, causal):
+    x = G.make_inputs(9300 + N + d, B, Hq, Hkv, N, d, dt, causal)
+    o_ref, l_ref = full_oracle(x)
+    o, l = run_gpu(x)
+    PT.compare(o, l, o_ref, l_ref, dt, False, f"{dt} N{N} d{d} causal={causal}")
+
+
 TILINGS_16 = [(128, 64), (64, 64), (128, 32), (256, 64)]
 
 
