@@ -82,6 +82,27 @@ def build(jobs: int | None = None, verbose: bool = False, lds_poison: bool = Fal
     return lib_path
 
 
+EXAMPLE_SRC = os.path.join(PKG, "example", "fa355_example.c")
+EXAMPLE_BIN = os.path.join(PKG, "fa355_example")
+
+
+def build_example(verbose: bool = False) -> str:
+    """Compile the C client of the library (HIP runtime + C ABI, no Python) next to
+    libfa355.so, which it finds through an $ORIGIN run path."""
+    clang = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "bin", "clang")
+    rocm = os.path.dirname(os.path.dirname(HIPCC))
+    cmd = [clang, "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", INCLUDE, EXAMPLE_SRC, "-o", EXAMPLE_BIN + ".tmp", "-L", PKG, "-lfa355",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("example build failed:\n" + r.stdout + r.stderr)
+    os.replace(EXAMPLE_BIN + ".tmp", EXAMPLE_BIN)
+    if verbose:
+        print(f"built {EXAMPLE_BIN}", flush=True)
+    return EXAMPLE_BIN
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
@@ -89,6 +110,8 @@ def main(argv=None) -> int:
     ap.add_argument("--lds-poison", action="store_true")
     a = ap.parse_args(argv)
     build(a.jobs, a.verbose, a.lds_poison)
+    if not a.lds_poison:
+        build_example(a.verbose)
     return 0
 
 
