@@ -317,6 +317,34 @@ def parity_of(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype: str, fp8: bool = False)
     return out
 
 
+def physical_cores() -> int | None:
+    """Distinct (package, core) pairs in /proc/cpuinfo (None if it cannot be read)."""
+    try:
+        pairs, phys = set(), None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "physical id":
+                    phys = val.strip()
+                elif key == "core id":
+                    pairs.add((phys, val.strip()))
+        return len(pairs) or None
+    except OSError:
+        return None
+
+
+def oracle_single_thread_small() -> float:
+    """Seconds for the oracle on the smallest workload (fp32 B1 H1 N128 d64) on one thread."""
+    import oracle
+    import fa_inputs as G
+    x = G.workload("f32_h1_n128_d64")
+    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, x.causal, x.scale, threads=1)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(x, budget_s: float = 15.0, gpu=None) -> dict:
     """Time the oracle on a bounded sample of the workload and scale to TFLOP/s.
 
@@ -372,7 +400,10 @@ def cpu_baseline(x, budget_s: float = 15.0, gpu=None) -> dict:
         sample = f"every {every}th query row of head (0,0) of {x.recipe}"
         pick = (0, slice(0, 1), rows)
     out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads"}
+           "sample": f"{sample}; {dt:.1f} s in fp64 on {threads} threads",
+           "host": {"threads_used": threads, "logical_cpus": os.cpu_count(),
+                    "physical_cores": physical_cores(),
+                    "single_thread_s_fp32_b1_h1_n128_d64": round(oracle_single_thread_small(), 6)}}
     if gpu is not None:
         o, lse, odt = gpu
         import torch  # noqa: F401 -- the GPU tensors are torch's
