@@ -232,10 +232,16 @@ def split_count(B: int, Hq: int, N: int, causal: bool, cus: int = 256, d: int = 
     """A split count that fills the GPU: about two workgroups per compute unit at
     head dim 128 (256-row tiles, one resident per CU) and four at 64 (128-row
     tiles), keeping at least four 64-key blocks per split (1 = no split).  On
-    B1 H2 N16384 d128 causal this picks 4; 3 to 6 measured within 2 % of each other."""
+    B1 H2 N16384 d128 causal this picks 4; 3 to 6 measured within 2 % of each other.
+    Without a mask, once the query tiles alone fill the GPU a split only adds the
+    partial results' round trip (B1 H8 N8192 d128: 256 us unsplit, 269 us in two
+    pieces), so it picks 1; causal tiles of unequal length still gain (B2 H8 N4096
+    d128 causal: 125 us unsplit, 97 us in two pieces)."""
     rows, per_cu = (256, 2) if d == 128 else (128, 4)
     tiles = B * Hq * ((N + rows - 1) // rows)
     if tiles == 0:                      # an empty call: nothing to split
+        return 1
+    if not causal and tiles >= cus:
         return 1
     want = -(-per_cu * cus // tiles)
     blocks = (N + 63) // 64

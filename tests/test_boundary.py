@@ -263,6 +263,8 @@ def test_split_count_heuristic():
     assert F.split_count(1, 32, 4096, True) == 1
     assert F.split_count(1, 1, 64, True) == 1
     assert F.split_count(1, 1, 8192, True) == 16        # 32 tiles: capped at 16
+    assert F.split_count(1, 8, 8192, False) == 1        # 256 tiles without a mask: no split
+    assert F.split_count(2, 8, 4096, True) == 2         # 256 causal tiles: still two pieces
     assert F.split_count(1, 1, 1 << 20, True) == 1      # 4096 tiles fill the GPU
     assert F.split_count(1, 1, 1024, False) == 4     # 16 key blocks: at most 4 splits
 
