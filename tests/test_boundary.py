@@ -301,6 +301,8 @@ def test_decode_split_count_heuristic():
     assert F.decode_split_count(1, 8, 4096) == 32          # one workgroup per CU
     assert F.decode_split_count(1, 1, 100) == 1            # at least four blocks a piece
     assert F.decode_split_count(1, 1, 1 << 22) == 256
+    assert F.decode_split_count(32, 8, 4096) == 2          # 256 (batch, head) pairs: 2 per CU
+    assert F.decode_split_count(64, 8, 2048) == 1
 
 
 def test_library_imports_no_allocating_or_copying_call():
