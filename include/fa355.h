@@ -38,6 +38,10 @@
  * Size limits (FA355_ERR_SHAPE beyond them): every tensor a call touches holds at
  * most 2^40 elements, and one head of each tensor fits the kernels' 32-bit byte
  * offsets (N d elem_bytes <= 2^31 - 1 - 65536; each entry point states its own).
+ * Each kernel launch a call makes must also have fewer than 2^32 work-items along
+ * each grid dimension (HIP's limit): e.g. the plain forward launches about
+ * 2 B Hq N work-items, the decoding merge 256 per (batch, head, query) row.  A
+ * call past that is FA355_ERR_SHAPE, found before any HIP call.
  * There is no silent fallback: an unsupported head dimension, dtype or tiling is an
  * error, never a slower path (contrast "FlashAttention…昇腾…" page 2, pitfall).
  */

@@ -102,6 +102,13 @@ bool too_large(int B, int H, int N, int d)
     return (unsigned __int128)B * (unsigned)H * (unsigned)N * (unsigned)d > kMaxElems;
 }
 
+// HIP counts the work-items of each grid dimension in 32 bits: a launch of `wgs`
+// workgroups of `threads` work-items along one dimension needs the product below 2^32.
+bool grid_fits(int64_t wgs, int threads)
+{
+    return wgs >= 0 && wgs <= (int64_t)UINT32_MAX / threads;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -172,7 +179,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
 
     const int64_t n_qtiles = (N + br - 1) / br;
     const int64_t tiles = (int64_t)B * Hq * n_qtiles;
-    if (tiles > INT_MAX)
+    if (tiles > INT_MAX || !grid_fits(tiles, 64 * var->waves))
         return FA355_ERR_SHAPE;
 
     fa355::FwdArgs &a = out.args;
@@ -280,7 +287,11 @@ int run_split(const void *q, const void *k, const void *v, void *o, float *lse, 
             return FA355_ERR_ARG;
     if (overlaps(o_part, bp, lse_part, bl))
         return FA355_ERR_ARG;
-    if ((int64_t)c.plan.grid * num_splits > INT_MAX)
+    // Partial-result launch: grid * num_splits workgroups of 64 * waves; merge launch:
+    // one 256-thread workgroup per 256 / (d / 4) rows.
+    if ((int64_t)c.plan.grid * num_splits > INT_MAX ||
+        !grid_fits((int64_t)c.plan.grid * num_splits, 64 * c.plan.waves) ||
+        !grid_fits(((int64_t)rows * (d / 4) + 255) / 256, 256))
         return FA355_ERR_SHAPE;
     const SplitVariant *var = nullptr;
     for (const SplitVariant &x : kSplitVariants)
@@ -418,6 +429,11 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     const int64_t n_tiles = (N + kBwdTile - 1) / kBwdTile;
     if ((int64_t)B * Hq * n_tiles > INT_MAX || (int64_t)B * Hq * N > INT_MAX)
         return FA355_ERR_SHAPE;
+    // delta: 256 / (d / 8) rows per 256-thread workgroup; dK/dV: one 256-thread
+    // workgroup per 128 keys; dQ: up to 512 threads per query tile.
+    if (!grid_fits(((int64_t)B * Hq * N * (d / 8) + 255) / 256, 256) ||
+        !grid_fits((int64_t)B * Hkv * n_tiles, 256) || !grid_fits((int64_t)B * Hq * n_tiles, 512))
+        return FA355_ERR_SHAPE;
 
     fa355::BwdArgs a;
     a.q = q;
@@ -487,7 +503,7 @@ int run_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
         return FA355_ERR_ARG;
     const int64_t n_qtiles = (N + kFp8Rows - 1) / kFp8Rows;
     const int64_t tiles = (int64_t)B * Hq * n_qtiles;
-    if (tiles > INT_MAX)
+    if (tiles > INT_MAX || !grid_fits(tiles, 256))
         return FA355_ERR_SHAPE;
 
     fa355::FwdArgs a = {};
@@ -568,7 +584,10 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
             if (overlaps(out[x].p, out[x].n, out[y].p, out[y].n))
                 return FA355_ERR_ARG;
     }
-    if ((int64_t)B * Hkv * num_splits > INT_MAX || (int64_t)rows > INT_MAX)
+    // Decode launch: one 64-thread workgroup per (batch, K/V head, piece); merge: one
+    // 256-thread workgroup per row along x.
+    if ((int64_t)B * Hkv * num_splits > INT_MAX || (int64_t)rows > INT_MAX ||
+        !grid_fits((int64_t)B * Hkv * num_splits, 64) || !grid_fits((int64_t)rows, 256))
         return FA355_ERR_SHAPE;
 
     float c = (float)(std::fabs((double)scale) * 1.4426950408889634);

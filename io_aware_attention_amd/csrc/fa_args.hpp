@@ -14,11 +14,11 @@
 namespace fa355 {
 
 // LDS bytes of a 16-bit-input kernel: two stages, each a K block (BC rows of D
-// values plus one 16-byte pad per row) and a V block (plus two pads per row), each
-// rounded up to whole 1 KB DMA instructions.
+// values plus one 16-byte pad per row, rounded up to whole 1 KB DMA instructions)
+// and an unpadded V block.
 constexpr int fwd_lds_bytes(int D, int BC)
 {
-    return 2 * 16 * ((BC * (D / 8 + 1) + 63) / 64 * 64 + (BC * (D / 8 + 2) + 63) / 64 * 64);
+    return 2 * 16 * ((BC * (D / 8 + 1) + 63) / 64 * 64 + BC * (D / 8));
 }
 
 struct FwdArgs {
@@ -71,6 +71,7 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+
 
 // Forward with an additive bias on the scaled scores.
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>

@@ -31,8 +31,8 @@
 // transposed, each lane owns one query row (its column), and a row's 2*16 scores sit
 // in lanes L and L^32: row reductions are in-lane plus one v_permlane32_swap.  The
 // same accumulator registers, converted to 16-bit, are directly the B operand of the
-// P.V product; V is stored transposed in LDS so that its A operand is one 16-byte
-// read per lane.
+// P.V product; V stays row-major in LDS and its A operand (Vᵀ fragments) comes from
+// transposing 8-byte LDS reads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -161,6 +161,35 @@ __device__ __forceinline__ u32x2_t read_tr16(const char *p) {
 #endif
 }
 
+// V blocks sit in LDS unpadded, with the 16-byte chunks of each key row permuted:
+// chunk c of row r is stored in slot c ^ v_swz(r).  The 32 lanes one transposed
+// 8-byte read serves per LDS cycle (256 bytes) cover key rows 4g .. 4g + 3 and one
+// 64-byte column group, chunks 4 nb .. 4 nb + 3; the XOR (bits 2-3 of the chunk index
+// only) sends those four rows to four different 64-byte groups of banks.  A 128-byte
+// row (head dim 64) shares its 64 banks with the next row, so there rows r and r + 2
+// are the ones to separate.
+template <int D>
+__device__ __forceinline__ int v_swz(int r)
+{
+    return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+}
+
+// Per-lane LDS offsets (from the start of a V block) of the transposed reads of the
+// 32-column blocks nb = q + 4 m (q < 4; add 256 m bytes): lane L reads key row
+// 4 (L / 32) + (L % 16) / 4 (+ 16 kstep, + 8), columns 16 ((L / 16) % 2) + 4 (L % 4)
+// .. + 3 of the block, i.e. 8 bytes at chunk 4 nb + 2 ((L / 16) % 2) + (L % 4) / 2,
+// byte 8 (L % 2) of that chunk.
+template <int D>
+__device__ __forceinline__ void v_read_offsets(int lane, int (&off)[(D / 32) < 4 ? (D / 32) : 4])
+{
+    const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int sw4 = v_swz<D>(r) >> 2;
+    const int base = r * 2 * D + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+#pragma unroll
+    for (int q = 0; q < ((D / 32) < 4 ? (D / 32) : 4); ++q)
+        off[q] = base + 64 * (q ^ sw4);
+}
+
 // Values of lanes L and L^32 (same query row), in a fixed order on both lanes.
 __device__ __forceinline__ f32x2_t row_pair(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -210,15 +239,15 @@ struct FwdTraits {
     static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     // K and V blocks go from global memory straight into LDS (no registers).
     // One 64-lane DMA instruction fills 64 consecutive 16-byte LDS slots, so a
-    // block is laid out in slots: K row j takes CPR slots plus one pad slot
-    // (rows start 4 banks apart: the 16-byte fragment reads of 8 consecutive rows
-    // hit distinct banks); V row j takes CPR slots plus two pad slots (rows start
-    // 8 banks apart: the four rows one transposed read touches hit distinct banks).
-    // Pad slots, and slots past the block, receive out-of-range (zero) loads.
+    // block is laid out in slots: K row j takes CPR slots plus one pad slot (rows
+    // start 4 banks apart: the 16 lanes one 16-byte read serves per LDS cycle, 16
+    // consecutive rows at one chunk, hit 16 distinct groups of 4 banks); V row j
+    // takes CPR slots, its chunks permuted by v_swz.  Pad slots, and slots past the
+    // block, receive out-of-range (zero) loads.
     static constexpr int K_PITCH = D * 2 + 16;
-    static constexpr int V_PITCH = D * 2 + 32;
+    static constexpr int V_PITCH = D * 2;
     static constexpr int K_SLOTS = (BC * (CPR + 1) + 63) / 64 * 64;
-    static constexpr int V_SLOTS = (BC * (CPR + 2) + 63) / 64 * 64;
+    static constexpr int V_SLOTS = BC * CPR;
     static constexpr int K_INSTR = K_SLOTS / 64;
     static constexpr int N_INSTR = (K_SLOTS + V_SLOTS) / 64;   // DMA instructions per block
     static constexpr int P_INSTR = (N_INSTR + WAVES - 1) / WAVES;  // per wavefront
@@ -306,11 +335,15 @@ fa_fwd_kernel(FwdArgs a)
 #pragma unroll
     for (int p = 0; p < Tr::P_INSTR; ++p) {
         const int i = p * WAVES + wave;
-        const bool isk = i < Tr::K_INSTR;
-        const int slot = (isk ? i : i - Tr::K_INSTR) * 64 + lane;
-        const int spr = isk ? Tr::CPR + 1 : Tr::CPR + 2;     // slots per row
-        const int row = slot / spr, ch = slot - row * spr;
-        dma_off[p] = (row < BC && ch < Tr::CPR) ? row * ROW + ch * 16 : 0x7ffffff0;
+        if (i < Tr::K_INSTR) {
+            const int slot = i * 64 + lane;
+            const int row = slot / (Tr::CPR + 1), ch = slot - row * (Tr::CPR + 1);
+            dma_off[p] = (row < BC && ch < Tr::CPR) ? row * ROW + ch * 16 : 0x7ffffff0;
+        } else {
+            const int slot = (i - Tr::K_INSTR) * 64 + lane;
+            const int row = slot / Tr::CPR, sl = slot - row * Tr::CPR;
+            dma_off[p] = row * ROW + 16 * (sl ^ v_swz<D>(row));
+        }
     }
 
     // Block t of K and V into LDS stage `stage`.  The block's rows start each
@@ -361,11 +394,11 @@ fa_fwd_kernel(FwdArgs a)
 
     // LDS read bases (per lane).  K: row l32, chunk h2 (16-byte reads).  V: the
     // transposed 64-bit read gives each 16-lane group a 4-key x 16-column block,
-    // lane L receiving column L % 16 of it; lane L addresses key row
-    // 4 * (L / 32) + (L % 16) / 4 and columns 16 * ((L / 16) % 2) + 4 * (L % 4).
+    // lane L receiving column L % 16 of it (v_read_offsets).
     const int k_rd = l32 * Tr::K_PITCH + h2 * 16;
-    const int v_rd = Tr::K_STAGE + (4 * h2 + ((lane & 15) >> 2)) * Tr::V_PITCH +
-                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    constexpr int VQ = Tr::NB < 4 ? Tr::NB : 4;
+    int v_rd[VQ];
+    v_read_offsets<D>(lane, v_rd);
 
     f32x16_t oacc[Tr::NB];
 #pragma unroll
@@ -404,7 +437,7 @@ fa_fwd_kernel(FwdArgs a)
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {
             const char *kb = smem + ((t - t_begin) & 1) * STAGE + k_rd;
-            const char *vb = smem + ((t - t_begin) & 1) * STAGE + v_rd;
+            const char *vs = smem + ((t - t_begin) & 1) * STAGE + Tr::K_STAGE;
 
             f32x16_t sacc[Tr::JB];
 #pragma unroll
@@ -543,7 +576,7 @@ fa_fwd_kernel(FwdArgs a)
 #pragma unroll
                 for (int kstep = 0; kstep < Tr::KS; ++kstep) {
                     // Keys 16 kstep + 4 (L/32) + 0..3 and the same + 8 of column n.
-                    const char *va = vb + kstep * 16 * Tr::V_PITCH + nb * 64;
+                    const char *va = vs + v_rd[nb & 3] + 256 * (nb >> 2) + kstep * 16 * Tr::V_PITCH;
                     const u32x2_t lo = read_tr16(va), hi = read_tr16(va + 8 * Tr::V_PITCH);
                     const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
                     oacc[nb] = M::run(vf, pf[kstep], oacc[nb]);

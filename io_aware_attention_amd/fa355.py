@@ -122,6 +122,39 @@ def _tuning(tuning):
     return ctypes.byref(Tuning(int(br), int(bc)))
 
 
+def _qkv_shapes(q, k, v, same_len: bool = True):
+    """(B, Hq, Hkv, N, Nk, d) of 4-D q [B,Hq,N,d] and k, v [B,Hkv,Nk,d] that agree in
+    B and d (and N = Nk when same_len), with one dtype; FA355Error otherwise."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FA355Error(ERR_SHAPE, "q, k, v must be 4-D [B,H,N,d]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape) or (same_len and Nk != N):
+        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
+    return B, Hq, Hkv, N, Nk, d
+
+
+def _given(name, t, shape, dtype):
+    """A caller-provided output or workspace must have exactly this shape and dtype
+    and be contiguous (the library writes it as a dense array of that size)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise FA355Error(ERR_ARG, f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} (got {t.dtype} {tuple(t.shape)})")
+
+
+def _on_device(device, **tensors):
+    """Every tensor handed to the library is a contiguous tensor on `device`."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.device != device:
+            raise FA355Error(ERR_ARG, f"{name} must be a contiguous tensor on {device}")
+
+
 def plan(B, Hq, Hkv, N, d, causal, dtype, out_dtype=None, tuning=None, scale=None) -> Plan:
     """The launch fa_fwd_ex would make for these sizes (no GPU needed)."""
     dt = _dtype_code(dtype)
@@ -150,29 +183,17 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out_dtype=
     """
     import torch
     L = lib()
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise FA355Error(ERR_SHAPE, "q, k, v must be 4-D [B,H,N,d]")
-    B, Hq, N, d = q.shape
-    Bk, Hkv, Nk, dk = k.shape
-    if (Bk, Nk, dk) != (B, N, d) or tuple(v.shape) != tuple(k.shape):
-        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    B, Hq, Hkv, N, _, d = _qkv_shapes(q, k, v)
     dt = _dtype_code(q.dtype)
     odt_t = q.dtype if out_dtype is None else out_dtype
     odt = _dtype_code(odt_t)
+    _given("o", o, (B, Hq, N, d), odt_t)
+    _given("lse", lse, (B, Hq, N), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
     if o is None:
         o = torch.empty((B, Hq, N, d), dtype=odt_t, device=q.device)
-    elif tuple(o.shape) != (B, Hq, N, d) or o.dtype != odt_t or not o.is_contiguous():
-        raise FA355Error(ERR_ARG, "o has the wrong shape, dtype or layout")
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if lse is not None and (tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32
-                            or not lse.is_contiguous()):
-        raise FA355Error(ERR_ARG, "lse has the wrong shape, dtype or layout")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream(q.device) if stream is None else stream
@@ -194,29 +215,22 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     """
     import torch
     L = lib()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
-        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
-        if tuple(t.shape) != tuple(shape) or t.dtype != q.dtype:
+    B, Hq, Hkv, N, _, d = _qkv_shapes(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
             raise FA355Error(ERR_SHAPE, f"{name} must match q in shape and dtype")
     if tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
         raise FA355Error(ERR_SHAPE, "lse must be fp32 [B,Hq,N]")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    _given("dq", dq, (B, Hq, N, d), torch.float32)
+    _given("dk", dk, (B, Hkv, N, d), torch.float32)
+    _given("dv", dv, (B, Hkv, N, d), torch.float32)
+    _given("delta", delta, (B, Hq, N), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty((B, Hq, N, d), **f32) if dq is None else dq
     dk = torch.empty((B, Hkv, N, d), **f32) if dk is None else dk
     dv = torch.empty((B, Hkv, N, d), **f32) if dv is None else dv
     delta = torch.empty((B, Hq, N), **f32) if delta is None else delta
-    for name, t, shape in (("dq", dq, (B, Hq, N, d)), ("dk", dk, (B, Hkv, N, d)),
-                           ("dv", dv, (B, Hkv, N, d)), ("delta", delta, (B, Hq, N))):
-        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} has the wrong shape, dtype or layout")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream(q.device) if stream is None else stream
@@ -257,14 +271,18 @@ def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, num_spl
     """
     import torch
     L = lib()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, N, _, d = _qkv_shapes(q, k, v)
+    _dtype_code(q.dtype)
     if num_splits is None:
         num_splits = split_count(B, Hq, N, causal, d=d)
     S = int(num_splits)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    if S < 1:
+        raise FA355Error(ERR_ARG, f"num_splits must be >= 1 (got {S})")
+    _given("o", o, (B, Hq, N, d), q.dtype)
+    _given("lse", lse, (B, Hq, N), torch.float32)
+    _given("o_part", o_part, (S, B, Hq, N, d), torch.float32)
+    _given("lse_part", lse_part, (S, B, Hq, N), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse, o_part=o_part, lse_part=lse_part)
     f32 = dict(dtype=torch.float32, device=q.device)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq, N), **f32) if lse is None else lse
@@ -291,8 +309,10 @@ def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, *,
     """
     import torch
     L = lib()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, N, _, d = _qkv_shapes(q, k, v)
+    _dtype_code(q.dtype)
+    _given("o", o, (B, Hq, N, d), q.dtype)
+    _given("lse", lse, (B, Hq, N), torch.float32)
     if bias.dim() != 4 or tuple(bias.shape[2:]) != (N, N) or bias.shape[0] not in (1, B) \
             or bias.shape[1] not in (1, Hq) or bias.dtype != q.dtype or bias.stride(3) != 1:
         raise FA355Error(ERR_SHAPE, f"bias {tuple(bias.shape)} does not fit [B,Hq,N,N] of q's dtype")
@@ -304,6 +324,9 @@ def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, *,
         padded = torch.zeros(tuple(bias.shape[:3]) + (Np,), dtype=bias.dtype, device=bias.device)
         padded[..., :N] = bias
         bias = padded[..., :N]
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    if not bias.is_cuda or bias.device != q.device:
+        raise FA355Error(ERR_ARG, f"bias must be a tensor on {q.device}")
     sb = 0 if bias.shape[0] == 1 else bias.stride(0)
     sh = 0 if bias.shape[1] == 1 else bias.stride(1)
     o = torch.empty_like(q) if o is None else o
@@ -330,19 +353,14 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
     """
     import torch
     L = lib()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
-        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, Hq, Hkv, N, _, d = _qkv_shapes(q, k, v)
     ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype not in ok:
-            raise FA355Error(ERR_UNSUPPORTED, f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn)")
-        if not t.is_cuda or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    if q.dtype not in ok:
+        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must hold e4m3 codes (uint8 or float8_e4m3fn)")
+    _given("o", o, (B, Hq, N, d), torch.bfloat16)
+    _given("lse", lse, (B, Hq, N), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
     o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device) if o is None else o
-    if tuple(o.shape) != (B, Hq, N, d) or o.dtype != torch.bfloat16 or not o.is_contiguous():
-        raise FA355Error(ERR_ARG, "o has the wrong shape, dtype or layout")
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -384,16 +402,16 @@ def fwd_decode(q, k, v, causal: bool = True, scale: float | None = None, num_spl
     """
     import torch
     L = lib()
-    B, Hq, Nq, d = q.shape
-    Bk, Hkv, Nk, dk = k.shape
-    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
-        raise FA355Error(ERR_SHAPE, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise FA355Error(ERR_UNSUPPORTED, "q, k, v must share a dtype")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise FA355Error(ERR_ARG, f"{name} must be a contiguous device tensor")
+    B, Hq, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v, same_len=False)
+    _dtype_code(q.dtype)
     S = int(decode_split_count(B, Hkv, Nk) if num_splits is None else num_splits)
+    if S < 1:
+        raise FA355Error(ERR_ARG, f"num_splits must be >= 1 (got {S})")
+    _given("o", o, (B, Hq, Nq, d), q.dtype)
+    _given("lse", lse, (B, Hq, Nq), torch.float32)
+    _given("o_part", o_part, (S, B, Hq, Nq, d), torch.float32)
+    _given("lse_part", lse_part, (S, B, Hq, Nq), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse, o_part=o_part, lse_part=lse_part)
     f32 = dict(dtype=torch.float32, device=q.device)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq, Nq), **f32) if lse is None else lse

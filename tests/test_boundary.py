@@ -52,13 +52,13 @@ def check(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE 
 def test_valid_call_plans_a_launch():
     rc, p = check(B_=1, Hq=32, Hkv=32, N=4096, d=128)
     assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (256, 64, 8, 512)
-    # two stages of 16-byte slots: K rows of 16 + 1 pad slots, V rows of 16 + 2,
-    # each block rounded up to whole 64-slot (1 KB) DMA instructions
+    # two stages of 16-byte slots: K rows of 16 + 1 pad slots (rounded up to whole
+    # 64-slot (1 KB) DMA instructions), unpadded V rows of 16 slots
     ceil64 = lambda n: (n + 63) // 64 * 64
-    assert p.lds_bytes == 2 * 16 * (ceil64(64 * 17) + ceil64(64 * 18)) == 71680
+    assert p.lds_bytes == 2 * 16 * (ceil64(64 * 17) + 64 * 16) == 67584
     rc, p = check(B_=1, Hq=32, Hkv=32, N=2048, d=128)
     assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 32, 4, 512)
-    assert p.lds_bytes == 2 * 16 * (ceil64(32 * 17) + ceil64(32 * 18)) == 36864
+    assert p.lds_bytes == 2 * 16 * (ceil64(32 * 17) + 32 * 16) == 34816
     rc, p = check(B_=4, Hq=32, Hkv=8, N=8192)
     assert rc == 0 and (p.br, p.bc, p.grid) == (256, 64, 4 * 32 * 32)
     rc, p = check(B_=1, Hq=1, Hkv=1, N=128, d=64, dt=F.F32, tuning=(32, 32))
@@ -84,6 +84,9 @@ def test_valid_call_plans_a_launch():
     (dict(d=96), -3), (dict(d=32), -3), (dict(d=512), -3), (dict(dt=F.F32, d=128), -3),
     (dict(dt=7), -3), (dict(odt=F.F16), -3), (dict(dt=F.F32, d=64, odt=F.BF16), -3),
     (dict(tuning=(96, 64)), -3), (dict(tuning=(128, 48)), -3),
+    # every launch stays below 2^32 work-items per grid dimension
+    (dict(B_=1024, Hq=1024, Hkv=1024, N=2048, d=64, q=1 << 44, k=2 << 44, v=3 << 44, o=4 << 44,
+          lse=5 << 44), -2),
     (dict(dt=F.F32, d=64, tuning=(128, 64)), -3),
     (dict(scale=float("inf")), -5), (dict(scale=float("nan")), -5),
     (dict(q=BASE + 2), -4), (dict(o=BASE + 3 * SPAN + 8), -4), (dict(lse=BASE + 4 * SPAN + 2), -4),
@@ -93,6 +96,26 @@ def test_valid_call_plans_a_launch():
 def test_rejections(kw, code):
     rc, _ = check(**kw)
     assert rc == code, (kw, rc)
+
+
+def test_grid_work_item_limit():
+    # 2^20 heads x 8 query tiles x 512 threads = 2^32 work-items: rejected; one head
+    # fewer fits.  Pointers are spaced 2^44 bytes apart (the tensors are 2^38 bytes).
+    far = dict(q=1 << 44, k=2 << 44, v=3 << 44, o=4 << 44, lse=5 << 44, N=2048, d=64)
+    assert check(B_=1024, Hq=1024, Hkv=1024, **far)[0] == -2
+    rc, p = check(B_=1024, Hq=1023, Hkv=1023, **far)
+    assert rc == 0 and p.grid * 64 * p.waves < 1 << 32
+    # Decoding: the merge launch has 256 work-items per (batch, head, query) row.
+    L = F.lib()
+    big = [ctypes.c_void_p(n << 44) for n in range(1, 8)]
+    rows_limit = (1 << 32) // 256                      # 2^24 rows
+    B_ = rows_limit // 32                              # Hq = 32, Nq = 1
+    assert L.fa_fwd_decode(big[0], big[1], big[2], big[3], big[4], B_, 32, 1, 1, 64, 64, 1, 0.1,
+                           F.BF16, 1, big[5], big[6], None) == -2
+    # Backward: dQ, dK/dV and delta launches are held to the same limit.
+    assert L.fa_bwd(*big[:5], ctypes.c_void_p(6 << 44), ctypes.c_void_p(8 << 44),
+                    ctypes.c_void_p(9 << 44), ctypes.c_void_p(10 << 44), ctypes.c_void_p(11 << 44),
+                    1 << 16, 1 << 10, 1 << 10, 256, 64, 1, 0.1, F.BF16, None) == -2
 
 
 def test_empty_calls_return_ok_without_touching_anything():
@@ -146,7 +169,11 @@ def test_tensors_above_2_40_elements_are_too_large():
     kw = dict(q=BASE, k=BASE + far, v=BASE + 2 * far, o=BASE + 3 * far, lse=BASE + 4 * far)
     assert check(**kw, B_=2048, Hq=4096, Hkv=4096, N=8192, d=128)[0] == -2      # 2^43
     assert check(**kw, B_=2**30, Hq=2**30, Hkv=2**30, N=4096, d=128)[0] == -2
-    assert check(**kw, B_=256, Hq=4096, Hkv=4096, N=8192, d=128)[0] == 0       # exactly 2^40
+    # Exactly 2^40 elements passes the size check, but its 2^25 workgroups of 512
+    # work-items exceed a grid dimension's 2^32; with 64-bit extents the overlap
+    # check still runs first (fake tensors 4 GiB apart overlap).
+    assert check(**kw, B_=256, Hq=4096, Hkv=4096, N=8192, d=128)[0] == -2
+    assert check(**kw, B_=2, Hq=4096, Hkv=4096, N=8192, d=128)[0] == 0        # 2^33 elements
     assert check(B_=256, Hq=4096, Hkv=4096, N=8192, d=128)[0] == -5            # 4 GiB apart: overlap
     L = F.lib()
     assert L.fa_fwd_bias(BASE, BASE + SPAN, BASE + 2 * SPAN, BASE + 3 * SPAN, BASE + 4 * SPAN,
@@ -336,3 +363,58 @@ def test_use_library_restores_the_previous_library():
         with B.use_library(B.LIB_PATH + ".missing"):
             pass
     assert B.lib() is before
+
+
+def test_binding_rejects_mismatched_tensors_before_any_launch():
+    # Every entry point of the binding checks the 4-D shapes of q, k, v and their
+    # agreement, one dtype, and the exact shape and dtype of any output or workspace
+    # it is given, before a device is touched: these raise on a machine without a GPU.
+    import torch
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.zeros(1, 4, 64, 128, **bf)
+    k = torch.zeros(1, 2, 64, 128, **bf)
+    short = torch.zeros(1, 2, 63, 128, **bf)
+    f32 = dict(dtype=torch.float32)
+
+    def raises(status, fn, *a, **kw):
+        with pytest.raises(F.FA355Error) as e:
+            fn(*a, **kw)
+        assert e.value.status == status, (fn.__name__, e.value)
+
+    for fn in (F.fwd, F.fwd_split):
+        raises(B.ERR_SHAPE, fn, q, short, short)                      # k shorter than q
+        raises(B.ERR_SHAPE, fn, q, k, short)                          # v unlike k
+        raises(B.ERR_SHAPE, fn, q[0], k, k)                           # not 4-D
+        raises(B.ERR_UNSUPPORTED, fn, q, k.half(), k)                 # mixed dtypes
+        raises(B.ERR_ARG, fn, q, k, k, o=torch.zeros(1, 4, 64, 64, **bf))
+        raises(B.ERR_ARG, fn, q, k, k, lse=torch.zeros(1, 4, 64, **bf))
+        raises(B.ERR_ARG, fn, q, k, k)                                # host tensors
+    raises(B.ERR_ARG, F.fwd_split, q, k, k, num_splits=4, o_part=torch.zeros(3, 1, 4, 64, 128, **f32))
+    raises(B.ERR_ARG, F.fwd_split, q, k, k, num_splits=4, lse_part=torch.zeros(4, 1, 4, 64, **bf))
+    raises(B.ERR_ARG, F.fwd_split, q, k, k, num_splits=0)
+    bias = torch.zeros(1, 1, 64, 64, **bf)
+    raises(B.ERR_SHAPE, F.fwd_bias, q, short, short, bias)
+    raises(B.ERR_UNSUPPORTED, F.fwd_bias, q, k, k.half(), bias)
+    raises(B.ERR_ARG, F.fwd_bias, q, k, k, bias, o=torch.zeros(1, 4, 64, 128, **f32))
+    raises(B.ERR_ARG, F.fwd_bias, q.transpose(2, 3).contiguous().transpose(2, 3), k, k, bias)
+    raises(B.ERR_SHAPE, F.fwd_bias, q, k, k, torch.zeros(1, 1, 64, 63, **bf))
+    u8 = dict(dtype=torch.uint8)
+    q8, k8 = torch.zeros(1, 4, 64, 128, **u8), torch.zeros(1, 2, 64, 128, **u8)
+    raises(B.ERR_SHAPE, F.fwd_fp8, q8, k8[:, :, :32], k8[:, :, :32], 1.0, 1.0, 1.0)
+    raises(B.ERR_UNSUPPORTED, F.fwd_fp8, q, k, k, 1.0, 1.0, 1.0)
+    raises(B.ERR_ARG, F.fwd_fp8, q8, k8, k8, 1.0, 1.0, 1.0, lse=torch.zeros(1, 4, 64, **bf))
+    raises(B.ERR_ARG, F.fwd_fp8, q8, k8, k8, 1.0, 1.0, 1.0, o=torch.zeros(1, 4, 64, 128, **f32))
+    # Decoding: queries and cache may differ in length, nothing else.
+    qd = torch.zeros(1, 8, 1, 128, **bf)
+    kd = torch.zeros(1, 2, 300, 128, **bf)
+    raises(B.ERR_SHAPE, F.fwd_decode, qd, kd, kd[:, :, :200])
+    raises(B.ERR_SHAPE, F.fwd_decode, qd, torch.zeros(2, 2, 300, 128, **bf), torch.zeros(2, 2, 300, 128, **bf))
+    raises(B.ERR_ARG, F.fwd_decode, qd, kd, kd, num_splits=8, o_part=torch.zeros(4, 1, 8, 1, 128, **f32))
+    raises(B.ERR_ARG, F.fwd_decode, qd, kd, kd, num_splits=8, lse_part=torch.zeros(8, 1, 8, 2, **f32))
+    raises(B.ERR_ARG, F.fwd_decode, qd, kd, kd, o=torch.zeros(1, 8, 1, 128, **f32))
+    # Backward: gradients and workspace must be fp32 of the exact shapes.
+    o, do, lse = torch.zeros_like(q), torch.zeros_like(q), torch.zeros(1, 4, 64, **f32)
+    raises(B.ERR_SHAPE, F.bwd, q, short, short, o, do, lse)
+    raises(B.ERR_ARG, F.bwd, q, k, k, o, do, lse, dk=torch.zeros(1, 4, 64, 128, **f32))
+    raises(B.ERR_ARG, F.bwd, q, k, k, o, do, lse, delta=torch.zeros(1, 4, 64, **bf))
+    raises(B.ERR_ARG, F.bwd, q, k, k, o, do, lse)                                 # host tensors

@@ -299,7 +299,7 @@ def test_empty_inputs():
                False, "after empty calls")
 
 
-@pytest.mark.parametrize("tl", [None, (128, 32), (64, 64)])
+@pytest.mark.parametrize("tl", [None, (128, 32), (64, 64), (256, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_growing_row_maximum(dt, tl):
     # Key rows scaled up along the sequence (up to 12x): in most rows the maximum
