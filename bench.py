@@ -55,39 +55,186 @@ METRIC_FP8 = "attention fwd TFLOP/s and % of MI355X fp8 MFMA peak (e4m3 inputs, 
 FP8_WORKLOAD = "e4m3_h32_n4096_d128_causal"
 METRIC_DECODE = "attention decode GB/s (K/V cache read) and % of MI355X HBM bandwidth"
 DECODE_WORKLOAD = "bf16_decode_b8_hq32_hkv8_nk8192_d128"
-DECODE_KERNEL_SOURCES = ("fa_decode_kernel.hpp", "fa_fwd_kernel.hpp", "fa_inst_decode.hip",
-                         "fa_args.hpp", "fa355.cpp")
 BWD_FLOP_RATIO = 2.5   # backward = 5 matrix products (S, dP, dV, dK, dQ) vs the forward's 2
 DEFAULT_WORKLOAD = "bf16_h32_n4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# The kernel and the host code that picks its launch (tile, grid).
-KERNEL_SOURCES = ("fa_fwd_kernel.hpp", "fa_launch.hpp", "fa_args.hpp", "fa355.cpp")
-FP8_KERNEL_SOURCES = ("fa_fp8_kernel.hpp", "fa_fwd_kernel.hpp", "fa_args.hpp", "fa355.cpp")
+CONFIG_WORKLOADS = ("f32_h1_n128_d64", "f16_b16_h16_n512_d64_qbias",
+                    "bf16_gqa_b4_hq32_hkv8_n8192_d128_causal", "bf16_h16_n32768_d128_causal_x3",
+                    "bf16_h8_n8192_d256_causal_x3")
 
 
-def kernel_sha(sources=KERNEL_SOURCES) -> str:
-    h = hashlib.sha256()
-    for f in sources:
-        with open(os.path.join(ROOT, "io_aware_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def _elf_sections(b: bytes):
+    """(name, offset, size, addr, type, link, entsize) of every section of an ELF64 image."""
+    import struct
+    shoff = struct.unpack_from("<Q", b, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+    raw = [struct.unpack_from("<IIQQQQIIQQ", b, shoff + i * shentsize) for i in range(shnum)]
+    stroff = raw[shstrndx][4]
+    out = []
+    for nm, typ, _flags, addr, off, size, link, _info, _align, entsize in raw:
+        name = b[stroff + nm:b.index(b"\0", stroff + nm)].decode()
+        out.append((name, off, size, addr, typ, link, entsize))
+    return out
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if still current."""
+def _code_object_symbols(co: bytes):
+    """{symbol: bytes} of the functions (their machine code) and objects (kernel
+    descriptors) of one AMDGPU code object."""
+    import struct
+    secs = _elf_sections(co)
+    out = {}
+    for name, off, size, _addr, typ, link, entsize in secs:
+        if typ != 2:                                   # SHT_SYMTAB
+            continue
+        stroff = secs[link][1]
+        for i in range(size // entsize):
+            st_name, st_info, _other, shndx, value, sz = struct.unpack_from("<IBBHQQ", co, off + i * entsize)
+            kind = st_info & 0xF
+            if kind not in (1, 2) or sz == 0 or shndx == 0 or shndx >= len(secs):
+                continue
+            sym = co[stroff + st_name:co.index(b"\0", stroff + st_name)].decode()
+            _n, soff, _s, saddr, _t, _l, _e = secs[shndx]
+            out[sym] = co[soff + value - saddr:soff + value - saddr + sz]
+    return out
+
+
+def kernel_code_hashes(lib_path: str) -> dict:
+    """sha256 (first 16 hex digits) of each gfx950 kernel's machine code together with
+    its kernel descriptor, read from the library's embedded device code objects.  Two
+    builds with the same hash for a kernel run the same instructions with the same
+    register and LDS allocation, whatever else changed in the sources."""
+    import struct
+    with open(lib_path, "rb") as fh:
+        so = fh.read()
+    fat = [(off, size) for name, off, size, *_ in _elf_sections(so) if name == ".hip_fatbin"]
+    hashes = {}
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    for off, size in fat:
+        blob = so[off:off + size]
+        pos = blob.find(magic)
+        while pos >= 0:
+            n = struct.unpack_from("<Q", blob, pos + 24)[0]
+            q = pos + 32
+            for _ in range(n):
+                eoff, esize, tlen = struct.unpack_from("<QQQ", blob, q)
+                triple = blob[q + 24:q + 24 + tlen].decode()
+                q += 24 + tlen
+                if "gfx950" in triple and esize:
+                    syms = _code_object_symbols(blob[pos + eoff:pos + eoff + esize])
+                    for sym, code in syms.items():
+                        if sym.endswith(".kd"):
+                            continue
+                        h = hashlib.sha256(code + syms.get(sym + ".kd", b""))
+                        hashes[sym] = h.hexdigest()[:16]
+            pos = blob.find(magic, pos + 1)
+    return hashes
+
+
+def fwd_kernel_symbol(dtype: str, d: int, bc: int, waves: int, causal: bool) -> str:
+    """Mangled name of the forward kernel a plan launches (bf16 output, no split, no bias)."""
+    t = {"bf16": "4BF16", "f16": "3F16"}[dtype]
+    return (f"_ZN5fa35513fa_fwd_kernelINS_{t}ELi{d}ELi{bc}ELi{waves}ELb{int(causal)}"
+            f"ELb0ELb0ELb0EEEvNS_7FwdArgsE")
+
+
+def load_traffic(workload: str, kernels=None):
+    """HBM bytes per launch from the committed counter summary, or None unless every
+    kernel the summary was taken on still has the machine code it had then (and,
+    when `kernels` is given, the summary covers exactly those kernels)."""
     try:
         with open(TRAFFIC_FILE) as fh:
-            t = json.load(fh)
+            e = json.load(fh).get(workload)
     except (OSError, ValueError):
         return None
-    e = t.get(workload)
-    srcs = (FP8_KERNEL_SOURCES if workload.startswith("e4m3") else
-            DECODE_KERNEL_SOURCES if "decode" in workload else KERNEL_SOURCES)
-    if not e or e.get("kernel_sha") != kernel_sha(srcs):
+    if not e:
+        return None
+    import io_aware_attention_amd as F
+    current = kernel_code_hashes(F.fa355.LIB_PATH)
+    recorded = e.get("kernels", {})
+    if not recorded or any(current.get(k) != h for k, h in recorded.items()):
+        return None
+    if kernels is not None and set(kernels) != set(recorded):
         return None
     return e.get("bytes_per_launch")
+
+
+def _pmc_rows(path: str):
+    """(kernel name, counter, value) per dispatch row of a rocprofv3 counter CSV."""
+    import csv
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            yield row.get("Kernel_Name", ""), row.get("Counter_Name", ""), float(row.get("Counter_Value", 0)), \
+                row.get("Dispatch_Id", "")
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, kernels: list, command: str) -> dict:
+    """Reduces two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)
+    of `bench.py --profile-run --workload W` to HBM bytes per launch, each counter
+    scaled by what it reads for the run's calibration copy of known size, and stores
+    them in profiles/traffic.json with the machine-code hash of every kernel counted."""
+    import io_aware_attention_amd as F
+
+    def per_kernel(path, counter):
+        by = {}
+        for name, cname, val, disp in _pmc_rows(path):
+            if cname != counter:
+                continue
+            by.setdefault(name, {}).setdefault(disp, 0.0)
+            by[name][disp] += val
+        return {k: sum(v.values()) / len(v) for k, v in by.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = 64 * 2 ** 20 * 4                      # the calibration copy: 64 Mi fp32
+    copy = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy:
+        raise RuntimeError(f"no calibration copy kernel among {sorted(fetch)}")
+    ck = copy[0]
+    ffac = copy_bytes / (fetch[ck] * 1024.0)
+    wfac = copy_bytes / (write[ck] * 1024.0)
+    hashes = kernel_code_hashes(F.fa355.LIB_PATH)
+    names = {}
+    fkib = wkib = 0.0
+    for sym in kernels:
+        demangled = [k for k in fetch if _matches(sym, k)]
+        if len(demangled) != 1:
+            raise RuntimeError(f"{sym}: no unique dispatch name among {sorted(fetch)}")
+        names[sym] = hashes[sym]
+        fkib += fetch[demangled[0]]
+        wkib += write[demangled[0]]
+    entry = {"kernels": names, "bytes_per_launch": int(round(fkib * 1024 * ffac + wkib * 1024 * wfac)),
+             "fetch_kib_per_dispatch": round(fkib, 1), "write_kib_per_dispatch": round(wkib, 1),
+             "fetch_factor": round(ffac, 4), "write_factor": round(wfac, 4),
+             "calibration": f"{ck.split('(')[0][:80]} copying {copy_bytes} bytes in the same run",
+             "command": command}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    table[workload] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return entry
+
+
+def _matches(sym: str, demangled: str) -> bool:
+    """Does a rocprofv3 (demangled) kernel name denote the mangled symbol `sym`?"""
+    import re
+    m = re.match(r"_ZN5fa355(\d+)(\w+?)I(.*)EEvNS_\d+\w+E$", sym)
+    if not m:
+        return False
+    base = sym[len("_ZN5fa355") + len(m.group(1)):len("_ZN5fa355") + len(m.group(1)) + int(m.group(1))]
+    if f"fa355::{base}<" not in demangled:
+        return False
+    args = re.findall(r"Li(\d+)E|Lb(\d)E|NS_\d+(\w+?)E", m.group(3))
+    want = []
+    for num, b, t in args:
+        want.append(num if num else ("true" if b == "1" else "false") if b else f"fa355::{t}")
+    got = demangled[demangled.index("<") + 1:demangled.rindex(">")]
+    return [g.strip() for g in got.split(",")] == want
 
 
 SETTLE_S = 0.25   # untimed launches before the warm-up steps: the clock ramps for ~20 ms
@@ -310,6 +457,8 @@ def parity_of(o_gpu, lse_gpu, o_ref, lse_ref, out_dtype: str, fp8: bool = False)
     out = {"max_abs_o": float(err.max()), "max_abs_lse": float(lerr.max())}
     if fp8:
         out["tolerance"] = "per-element bounds from the e4m3 rounding (GPU tests)"
+        out["lse_err_over_1e-3"] = round(out["max_abs_lse"] / 1e-3, 3)
+        out["lse_within_1e-3"] = bool((lerr <= 1e-3).all())
         return out
     bound = 1e-5 if out_dtype == "f32" else 2e-2 + _half_ulp(o_ref, out_dtype)
     out["worst_o_err_over_tolerance"] = float((err / bound).max())
@@ -472,6 +621,29 @@ def cpu_baseline_decode(x, gpu=None) -> dict:
     return out
 
 
+def decode_kernels(x) -> list:
+    """Mangled names of the two kernels one decoding call launches."""
+    t = {"bf16": "4BF16", "f16": "3F16"}[x.dtype]
+    return [f"_ZN5fa35516fa_decode_kernelINS_{t}ELi{x.d}ELb{int(x.causal)}EEEvNS_10DecodeArgsE",
+            f"_ZN5fa35522fa_decode_merge_kernelINS_{t}ELi{x.d}EEEvNS_7FwdArgsE"]
+
+
+def fwd_kernels(x, plan) -> list:
+    """Mangled name of the forward kernel a workload launches (plan: fa_fwd_check's)."""
+    if x.dtype == "e4m3":
+        return [f"_ZN5fa35517fa_fwd_fp8_kernelILi{x.d}ELb{int(x.causal)}ELi4EEEvNS_7FwdArgsE"]
+    if x.dtype == "f32":
+        return [f"_ZN5fa35517fa_fwd_f32_kernelILi{plan.waves}ELb{int(x.causal)}EEEvNS_7FwdArgsE"]
+    return [fwd_kernel_symbol(x.dtype, x.d, plan.bc, plan.waves, x.causal)]
+
+
+def code_provenance(kernels: list) -> dict:
+    """The machine-code hash of each kernel the line timed, from the loaded library."""
+    import io_aware_attention_amd as F
+    h = kernel_code_hashes(F.fa355.LIB_PATH)
+    return {k: h.get(k) for k in kernels}
+
+
 def run_decode(args) -> dict:
     import torch
 
@@ -542,14 +714,88 @@ def run_decode(args) -> dict:
                            "query-head groups over key pieces, then the merge kernel)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": load_traffic(args.workload),
+                     "traffic": load_traffic(args.workload, decode_kernels(x)),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    line["roofline"]["kernel_code"] = code_provenance(decode_kernels(x))
     line["settle"] = {"seconds": SETTLE_S, "launches": settled}
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes, 1e-3, PEAK_HBM_GBS, cold=True)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_decode(x, gpu=(o, lse))
     return line
+
+
+def sampled_rows(N: int, br: int) -> "np.ndarray":
+    """Query rows checked against the oracle for a config line: the first rows, both
+    sides of the first tile boundary, the middle and the last rows."""
+    import numpy as np
+    rows = {0, 1, 2, br - 1, br, br + 1, N // 2, N - 2, N - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < N), dtype=np.int64)
+
+
+def measure_config(name: str, dev, stream) -> dict:
+    """Per-launch time of the forward pass on one more named workload (its default
+    launch), its rate against its roofline, and the GPU's error on sampled rows of
+    two heads against the fp64 oracle."""
+    import numpy as np
+    import torch
+
+    import fa_inputs as G
+    import io_aware_attention_amd as F
+    import oracle
+    from fa_inputs import storage_to_f64
+
+    x = G.workload(name)
+    tuning = G.WORKLOADS[name].get("tuning")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.dtype]
+    plan = F.plan(x.B, x.Hq, x.Hkv, x.N, x.d, x.causal, tdt, tuning=tuning, scale=x.scale)
+    q, k, v = device_inputs(x, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((x.B, x.Hq, x.N), dtype=torch.float32, device=dev)
+
+    def step():
+        F.fwd(q, k, v, causal=x.causal, scale=x.scale, o=o, lse=lse, tuning=tuning, stream=stream)
+
+    sync = lambda: torch.cuda.synchronize(dev)  # noqa: E731
+    settle(step, sync, 0.1)
+    med, mn = per_launch_us(step, stream, 50)
+    nbytes = x.q.nbytes + x.k.nbytes + x.v.nbytes + o.numel() * o.element_size() + x.B * x.Hq * x.N * 4
+    peak_flops = PEAK_TFLOPS[x.dtype]
+    if x.flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound, unit, peak, work, scale_ = "hbm", "GB/s", PEAK_HBM_GBS, nbytes, 1e-3
+    else:
+        bound, unit, peak, work, scale_ = "mfma", "TFLOP/s", peak_flops, x.flops, 1e-6
+    out = {"workload": name, "tile": [plan.br, plan.bc], "kernel_us": round(med, 2),
+           "kernel_us_min": round(mn, 2), "bound": bound, "achieved": round(work / med * scale_, 2),
+           "unit": unit, "peak": peak, "frac": round(work / med * scale_ / peak, 4),
+           "tflops": round(x.flops / med * 1e-6, 2),
+           "kernel_code": code_provenance(fwd_kernels(x, plan))}
+    if bound == "hbm":
+        cmed, cmn = per_launch_us(step, stream, 50, flush=cache_flusher(dev))
+        out["cold"] = {"kernel_us": round(cmed, 2), "achieved": round(work / cmed * scale_, 2),
+                       "frac": round(work / cmed * scale_ / peak, 4),
+                       "how": "a 512 MB buffer read before each launch, the reads timed alone and subtracted"}
+    # The oracle on sampled rows of the first and the last query head.
+    step()
+    sync()
+    rows = sampled_rows(x.N, plan.br)
+    G_ = x.Hq // x.Hkv
+    errs = []
+    for b, h in ((0, 0), (x.B - 1, x.Hq - 1)):
+        f64 = lambda n, hh: storage_to_f64(np.ascontiguousarray(getattr(x, n)[b:b + 1, hh:hh + 1]), x.dtype)  # noqa: E731
+        o_ref, l_ref = oracle.attention(f64("q", h), f64("k", h // G_), f64("v", h // G_), x.causal,
+                                        x.scale, rows=rows)
+        ri = torch.from_numpy(rows).to(dev)
+        og = o[b, h].index_select(0, ri).float().cpu().double().numpy()
+        lg = lse[b, h].index_select(0, ri).cpu().double().numpy()
+        errs.append(parity_of(og, lg, o_ref[0, 0], l_ref[0, 0], x.dtype))
+    out["parity"] = {"rows": f"{len(rows)} rows of heads (0,0) and ({x.B - 1},{x.Hq - 1})",
+                     "max_abs_o": max(e["max_abs_o"] for e in errs),
+                     "max_abs_lse": max(e["max_abs_lse"] for e in errs),
+                     "within_tolerance": all(e["within_tolerance"] for e in errs)}
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def run(args) -> dict:
@@ -676,9 +922,11 @@ def run(args) -> dict:
                    "grid": x.B * x.Hq * -(-x.N // 128) if fp8 else plan.grid},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None if args.bwd else load_traffic(args.workload),
+                     "traffic": None if args.bwd else load_traffic(args.workload, fwd_kernels(x, plan)),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if not args.bwd and args.split is None and args.bias is None:
+        line["roofline"]["kernel_code"] = code_provenance(fwd_kernels(x, plan))
     if args.bias is not None:
         line["config"]["pass"] = f"forward with an additive bias (fa_fwd_bias, bias {list(shape)})"
         line["config"].pop("tile"), line["config"].pop("waves"), line["config"].pop("grid")
@@ -697,6 +945,11 @@ def run(args) -> dict:
     line["settle"] = {"seconds": SETTLE_S, "launches": settled}
     add_protocol_fields(line, step, stream, dev, args.steps, nbytes if bound == "hbm" else flops,
                         1e-3 if bound == "hbm" else 1e-6, peak, cold=bound == "hbm")
+    if args.configs and not (args.bwd or fp8 or args.split is not None or args.bias is not None):
+        del q, k, v
+        torch.cuda.empty_cache()
+        line["configs"] = [measure_config(name, dev, stream) for name in CONFIG_WORKLOADS
+                           if name != args.workload]
     if not args.no_cpu:
         # The bias line times the same oracle without its bias: no parity there.
         odt = "bf16" if fp8 else x.dtype
@@ -704,6 +957,24 @@ def run(args) -> dict:
         line["cpu_baseline"] = (cpu_baseline_bwd(x, args.cpu_seconds) if args.bwd
                                 else cpu_baseline(x, args.cpu_seconds, gpu=gpu))
     return line
+
+
+def record_traffic_for(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
+    """record_traffic for the kernels a named workload's default launch uses."""
+    import fa_inputs as G
+    import io_aware_attention_amd as F
+    if "decode" in workload:
+        kernels = decode_kernels(G.workload(workload))
+    else:
+        x = G.workload(workload)
+        plan = None
+        if x.dtype != "e4m3":
+            import torch
+            tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.dtype]
+            plan = F.plan(x.B, x.Hq, x.Hkv, x.N, x.d, x.causal, tdt,
+                          tuning=G.WORKLOADS[workload].get("tuning"), scale=x.scale)
+        kernels = fwd_kernels(x, plan)
+    return record_traffic(workload, fetch_csv, write_csv, kernels, command)
 
 
 def main(argv=None) -> int:
@@ -728,7 +999,19 @@ def main(argv=None) -> int:
                          f"{DECODE_WORKLOAD} (--split sets the key pieces)")
     ap.add_argument("--fp8", action="store_true",
                     help=f"time the e4m3-input forward (fa_fwd_fp8) on {FP8_WORKLOAD}")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the per-launch timing of the other named workloads")
+    ap.add_argument("--record-traffic", metavar="WORKLOAD", default=None,
+                    help="reduce two rocprofv3 counter CSVs (--fetch-csv, --write-csv) of "
+                         "`--profile-run --workload WORKLOAD` into profiles/traffic.json")
+    ap.add_argument("--fetch-csv", default=None)
+    ap.add_argument("--write-csv", default=None)
+    ap.add_argument("--command", default="", help="the profiling command, stored with the entry")
     args = ap.parse_args(argv)
+    if args.record_traffic:
+        print(json.dumps(record_traffic_for(args.record_traffic, args.fetch_csv, args.write_csv,
+                                            args.command)), flush=True)
+        return 0
     if args.fp8:
         if args.bwd or args.split is not None or args.bias is not None:
             ap.error("--fp8 times the forward pass alone")

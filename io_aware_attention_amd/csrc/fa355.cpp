@@ -61,8 +61,8 @@ int empty_call(int B, int Hq, int Hkv, int N)
 // chosen by measurement on MI355X (interleaved timings on one device).  From 4096
 // tokens at head dim 128, 256 query rows share each 64-key block (the K/V loads and
 // the per-block bookkeeping are spread over more rows: 140 us against 144 us for
-// 128 x 32 on the causal B1 H32 N4096 layer); shorter sequences keep 128-row tiles
-// with 32-key blocks, whose lower register use fits three wavefronts per SIMD.
+// 128 x 32 on the causal B1 H32 N4096 layer); shorter sequences keep 128-row tiles,
+// whose lower register use fits more wavefronts per SIMD.
 void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
 {
     if (dt == FA355_F32) {
@@ -72,11 +72,12 @@ void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
         br = 128;
         bc = 64;
     } else if (d == 128) {
-        // 256 x 64 from N = 4096 (causal) or N = 2048 (no mask), 128 x 32 below
-        // (measured on MI355X, interleaved: non-causal N = 2048 142 against 145 us).
+        // 256 x 64 from N = 4096 (causal) or N = 2048 (no mask), 128 x 64 below
+        // (causal N = 2048: 51.4 against 53.9 us for 128 x 32; no mask, N = 1024:
+        // 24.3 against 26.2 us; no mask, N = 2048: 256 x 64 69.6 against 73.0 us).
         const bool wide = N >= 4096 || (!causal && N >= 2048);
         br = wide ? 256 : 128;
-        bc = wide ? 64 : 32;
+        bc = 64;
     } else if (dt == FA355_BF16) {
         // d = 64, bf16 (two wavefronts per SIMD for every tile; measured on MI355X,
         // interleaved): 256 x 64 without a mask (4-8 % ahead from N = 512 up), and
@@ -85,9 +86,17 @@ void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
         br = wide ? 256 : 128;
         bc = wide ? 64 : 32;
     } else {
-        // d = 64, fp16: 128 x 64 runs four wavefronts per SIMD and is ahead or even.
-        br = 128;
-        bc = 64;
+        // d = 64, fp16 (four wavefronts per SIMD at 128 rows): without a mask 128 x 32
+        // below N = 2048 (B16 H16 N512: 27.2 against 28.3 us for 128 x 64) and 256 x 64
+        // from it (B1 H16 N8192: 288 against 307 us); causal 128 x 32 below 4096 (N512:
+        // 20.9 against 21.9 us) and 128 x 64 from it (N8192: 174.4 against 175.3 us).
+        if (!causal) {
+            br = N >= 2048 ? 256 : 128;
+            bc = N >= 2048 ? 64 : 32;
+        } else {
+            br = 128;
+            bc = N >= 4096 ? 64 : 32;
+        }
     }
 }
 

@@ -57,7 +57,9 @@ def test_valid_call_plans_a_launch():
     ceil64 = lambda n: (n + 63) // 64 * 64
     assert p.lds_bytes == 2 * 16 * (ceil64(64 * 17) + 64 * 16) == 67584
     rc, p = check(B_=1, Hq=32, Hkv=32, N=2048, d=128)
-    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 32, 4, 512)
+    assert rc == 0 and (p.br, p.bc, p.waves, p.grid) == (128, 64, 4, 512)
+    assert p.lds_bytes == 2 * 16 * (ceil64(64 * 17) + 64 * 16) == 67584
+    rc, p = check(B_=1, Hq=32, Hkv=32, N=2048, d=128, tuning=(128, 32))
     assert p.lds_bytes == 2 * 16 * (ceil64(32 * 17) + 32 * 16) == 34816
     rc, p = check(B_=4, Hq=32, Hkv=8, N=8192)
     assert rc == 0 and (p.br, p.bc, p.grid) == (256, 64, 4 * 32 * 32)
@@ -65,14 +67,18 @@ def test_valid_call_plans_a_launch():
     assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
     rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
     assert rc == 0 and (p.br, p.bc) == (128, 64)
-    # d = 64: fp16 keeps 128 x 64; bf16 takes 256 x 64, except causal rows below 2048.
-    assert check(d=64, N=512, dt=F.F16, causal=0)[1].br == 128
+    # d = 64: fp16 takes 128 x 32 for short rows, 256 x 64 without a mask from 2048 and
+    # 128 x 64 with one from 4096; bf16 takes 256 x 64, except causal rows below 2048.
+    f16 = lambda N, c: (check(d=64, N=N, dt=F.F16, causal=c)[1].br, check(d=64, N=N, dt=F.F16, causal=c)[1].bc)
+    assert f16(512, 0) == (128, 32) and f16(2047, 0) == (128, 32) and f16(2048, 0) == (256, 64)
+    assert f16(512, 1) == (128, 32) and f16(4095, 1) == (128, 32) and f16(4096, 1) == (128, 64)
     assert (check(d=64, N=512, causal=0)[1].br, check(d=64, N=512, causal=0)[1].bc) == (256, 64)
     assert (check(d=64, N=2047, causal=1)[1].br, check(d=64, N=2047, causal=1)[1].bc) == (128, 32)
     assert (check(d=64, N=2048, causal=1)[1].br, check(d=64, N=2048, causal=1)[1].bc) == (256, 64)
-    # d = 128: 256 x 64 from N = 4096, or from N = 2048 without a mask.
+    # d = 128: 256 x 64 from N = 4096, or from N = 2048 without a mask; 128 x 64 below.
     assert check(N=2048, causal=1)[1].br == 128 and check(N=2048, causal=0)[1].br == 256
     assert check(N=2047, causal=0)[1].br == 128 and check(N=4096, causal=1)[1].br == 256
+    assert check(N=100, causal=1)[1].bc == 64 and check(N=4095, causal=1)[1].bc == 64
     rc, p = check(lse=None)
     assert rc == 0
 

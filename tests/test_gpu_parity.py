@@ -71,12 +71,16 @@ def test_small_full_parity(cfg):
 
 
 # Either side of the sequence lengths where the default tile changes (bf16 at d = 64
-# causal: 128 x 32 below 2048, 256 x 64 from it; d = 128 without a mask: the same
-# switch at 2048; d = 128 causal: at 4096), each with a ragged last tile.
+# causal: 128 x 32 below 2048, 256 x 64 from it; d = 128 without a mask: 128 x 64
+# below 2048, 256 x 64 from it; d = 128 causal: the same switch at 4096; fp16 at
+# d = 64: 128 x 32 below 2048 without a mask and below 4096 causal), each with a
+# ragged last tile.
 SWITCH = [
     (1, 2, 2, 2047, 64, "bf16", True), (1, 2, 2, 2048, 64, "bf16", True),
     (1, 2, 1, 2047, 128, "bf16", False), (1, 2, 1, 2048, 128, "f16", False),
     (1, 2, 2, 4095, 128, "bf16", True), (1, 2, 2, 4097, 128, "bf16", True),
+    (1, 2, 1, 2047, 64, "f16", False), (1, 2, 1, 2049, 64, "f16", False),
+    (1, 2, 2, 4095, 64, "f16", True), (1, 2, 2, 4097, 64, "f16", True),
 ]
 
 
