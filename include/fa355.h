@@ -29,7 +29,7 @@
  * pointers.  Asynchrony: a successful call enqueues exactly one kernel on `stream`
  * (NULL = the null stream) and returns; results are valid once the stream has
  * reached that point.  Calls are reentrant and thread-safe; the library keeps no
- * mutable state.  Errors: arguments are validated before any HIP call; on any
+ * mutable state apart from fa_fwd_decode_noalloc's per-GPU workspace.  Errors: arguments are validated before any HIP call; on any
  * error the call returns a negative fa355_status and leaves o and lse untouched.
  * Empty calls: with no query rows (B = 0, or N = 0; Nq = 0 for fa_fwd_decode) every
  * entry point returns FA355_OK at once, enqueues nothing and touches no buffer, so
@@ -242,6 +242,28 @@ int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *l
                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                   fa355_dtype dtype, int num_splits, float *o_part, float *lse_part,
                   hipStream_t stream);
+
+/*
+ * fa_fwd_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The partial results go to a workspace the library holds in a
+ * static device array of FA355_NOALLOC_SCRATCH_BYTES per GPU (each GPU the library
+ * runs on keeps its copy until the process ends): num_splits*B*Hq*Nq*d fp32 partial
+ * outputs, rounded up to 256 bytes, then num_splits*B*Hq*Nq fp32 partial lse values.
+ * A call whose workspace would exceed that size returns FA355_ERR_SHAPE before any
+ * HIP call.  Arguments, layouts, results and the kernels run are those of
+ * fa_fwd_decode; the workspace needs no clearing (every entry the merge reads is
+ * written by the same call).  Calls nothing that allocates (no hipMalloc, no hipFree);
+ * the workspace used is that of the GPU `stream` runs on, its address looked up on the
+ * first call for that GPU (FA355_ERR_HIP if the lookup fails).  All calls on one GPU
+ * share its workspace: calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race and may return
+ * each other's partial results; serialise them, e.g. on one stream.
+ */
+#define FA355_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_fwd_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, fa355_dtype dtype, int num_splits, hipStream_t stream);
 
 /* A static, human-readable name for a status code ("unknown status" otherwise). */
 const char *fa_status_str(int status);

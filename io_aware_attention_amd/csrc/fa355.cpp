@@ -2,14 +2,18 @@
 //
 // Validation runs completely before any HIP call, so every error leaves the
 // outputs untouched and can be exercised on a machine without a GPU.  A valid
-// call enqueues exactly one kernel and allocates nothing.
+// call enqueues its kernels (one, or two for the split-key paths) and allocates
+// nothing.
 #include "fa355.h"
+
+#include <hip/hip_runtime.h>
 
 #include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "fa_args.hpp"
 
@@ -550,11 +554,58 @@ int run_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
 
 constexpr int kMaxDecodeSplits = 256;
 
+// Workspace of fa_fwd_decode_noalloc: the per-piece partial results (fp32 O, then
+// lse at the next 256-byte boundary), in device memory the library owns -- one copy
+// per GPU, kept until the process ends.  Every call on a GPU uses that GPU's copy.
+static __device__ __align__(256) unsigned char scratch[FA355_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the GPU that `stream` runs on, looked up on the first
+// call for that GPU (with it made current for the lookup) and kept.  In host code the
+// array's name is only a host-side handle, never a device address.
+int scratch_for_stream(hipStream_t stream, unsigned char **out)
+{
+    static std::mutex mu;
+    static unsigned char *ptr[kMaxDevices] = {};
+    hipDevice_t dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return FA355_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess)
+            return FA355_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return FA355_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess)
+            return FA355_ERR_HIP;
+        if (e != hipSuccess || !p)
+            return FA355_ERR_HIP;
+        ptr[dev] = static_cast<unsigned char *>(p);
+    }
+    *out = ptr[dev];
+    return FA355_OK;
+}
+
+// Bytes of the no-allocation workspace a decoding call needs: S B Hq Nq d fp32 partial
+// outputs, then (256-byte aligned) S B Hq Nq fp32 partial lse values.
+uint64_t decode_scratch_bytes(int B, int Hq, int Nq, int d, int S)
+{
+    const uint64_t rows = (uint64_t)S * (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq;
+    return (rows * (uint64_t)d * 4 + 255) / 256 * 256 + rows * 4;
+}
+
+// own_scratch: the partial results go to `scratch` (o_part and lse_part are ignored
+// and computed here, after every check has passed).
 int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dt,
-               int num_splits, float *o_part, float *lse_part, hipStream_t stream)
+               int num_splits, float *o_part, float *lse_part, hipStream_t stream,
+               bool own_scratch = false)
 {
-    if (!q || !k || !v || !o || !o_part || !lse_part)
+    if (!q || !k || !v || !o || (!own_scratch && (!o_part || !lse_part)))
         return FA355_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0 || (causal && Nq > Nk))
         return FA355_ERR_SHAPE;
@@ -573,7 +624,9 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
         return FA355_ERR_ARG;
     if (num_splits < 1 || num_splits > kMaxDecodeSplits)
         return FA355_ERR_ARG;
-    const void *al16[] = {q, k, v, o, o_part};
+    if (own_scratch && decode_scratch_bytes(B, Hq, Nq, d, num_splits) > FA355_NOALLOC_SCRATCH_BYTES)
+        return FA355_ERR_SHAPE;
+    const void *al16[] = {q, k, v, o, own_scratch ? nullptr : o_part};
     for (const void *p : al16)
         if (reinterpret_cast<uintptr_t>(p) % 16)
             return FA355_ERR_ALIGN;
@@ -584,7 +637,9 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
     const size_t bp = (size_t)num_splits * rows * d * 4, bl = (size_t)num_splits * rows * 4;
     struct Span { const void *p; size_t n; };
     const Span in[] = {{q, nq}, {k, nkv}, {v, nkv}};
-    const Span out[] = {{o, nq}, {lse, lse ? rows * 4 : 0}, {o_part, bp}, {lse_part, bl}};
+    // The library's own workspace cannot overlap a caller's buffer.
+    const Span out[] = {{o, nq}, {lse, lse ? rows * 4 : 0}, {o_part, own_scratch ? 0 : bp},
+                        {lse_part, own_scratch ? 0 : bl}};
     for (size_t x = 0; x < 4; ++x) {
         for (const Span &i : in)
             if (overlaps(out[x].p, out[x].n, i.p, i.n))
@@ -599,6 +654,15 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
         !grid_fits((int64_t)B * Hkv * num_splits, 64) || !grid_fits((int64_t)rows, 256))
         return FA355_ERR_SHAPE;
 
+    // Every check has passed: now (and only now) the no-allocation path looks up its
+    // workspace on the current GPU.
+    if (own_scratch) {
+        unsigned char *sp = nullptr;
+        if (const int e = scratch_for_stream(stream, &sp); e != FA355_OK)
+            return e;
+        o_part = reinterpret_cast<float *>(sp);
+        lse_part = reinterpret_cast<float *>(sp + (bp + 255) / 256 * 256);
+    }
     float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
     if (!(c >= 1.17549435e-38f))
         c = 1.17549435e-38f;
@@ -756,6 +820,18 @@ int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *l
         return e;
     return run_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
                       o_part, lse_part, stream);
+}
+
+int fa_fwd_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, fa355_dtype dtype, int num_splits, hipStream_t stream)
+{
+    if (Nk < 0)
+        return FA355_ERR_SHAPE;
+    if (const int e = empty_call(B, Hq, Hkv, Nq); e <= 0)
+        return e;
+    return run_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
+                      nullptr, nullptr, stream, true);
 }
 
 int fa_version(void) { return 150; }

@@ -25,7 +25,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ARG, ERR_HIP = 0, -1, -
 
 # Every exported symbol, as declared in include/fa355.h.
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_fwd_split", "fa_fwd_bias", "fa_bwd",
-           "fa_fwd_fp8", "fa_fwd_decode", "fa_status_str", "fa_version")
+           "fa_fwd_fp8", "fa_fwd_decode", "fa_fwd_decode_noalloc", "fa_status_str",
+           "fa_version")
 
 
 class FA355Error(RuntimeError):
@@ -70,6 +71,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.fa_fwd_fp8.restype = ip
     L.fa_fwd_decode.argtypes = [vp] * 5 + [ip] * 7 + [fp, ip, ip, vp, vp, vp]
     L.fa_fwd_decode.restype = ip
+    L.fa_fwd_decode_noalloc.argtypes = [vp] * 5 + [ip] * 7 + [fp, ip, ip, vp]
+    L.fa_fwd_decode_noalloc.restype = ip
     L.fa_status_str.argtypes = [ip]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -423,5 +426,45 @@ def fwd_decode(q, k, v, causal: bool = True, scale: float | None = None, num_spl
     rc = L.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                          B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), _dtype_code(q.dtype),
                          S, o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    _check(rc)
+    return o, lse
+
+
+# Size of the library's own decoding workspace on each GPU (fa_fwd_decode_noalloc).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc_bytes(B: int, Hq: int, Nq: int, d: int, num_splits: int) -> int:
+    """Workspace bytes fwd_decode_noalloc needs: the fp32 partial outputs rounded up
+    to 256 bytes, then the fp32 partial lse values."""
+    rows = num_splits * B * Hq * Nq
+    return (rows * d * 4 + 255) // 256 * 256 + rows * 4
+
+
+def fwd_decode_noalloc(q, k, v, o, lse=None, causal: bool = True, scale: float | None = None,
+                       num_splits=None, *, stream=None):
+    """fwd_decode writing into the caller's o (and lse, if given) with the partial
+    results in the library's static per-GPU workspace: neither the library nor this
+    binding allocates device memory.  Calls that overlap in time on one GPU share
+    that workspace and race.  Returns (o, lse)."""
+    import torch
+    L = lib()
+    B, Hq, Hkv, Nq, Nk, d = _qkv_shapes(q, k, v, same_len=False)
+    _dtype_code(q.dtype)
+    S = int(decode_split_count(B, Hkv, Nk) if num_splits is None else num_splits)
+    if S < 1:
+        raise FA355Error(ERR_ARG, f"num_splits must be >= 1 (got {S})")
+    if o is None:
+        raise FA355Error(ERR_ARG, "fwd_decode_noalloc writes into a given o")
+    _given("o", o, (B, Hq, Nq, d), q.dtype)
+    _given("lse", lse, (B, Hq, Nq), torch.float32)
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    rc = L.fa_fwd_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 None if lse is None else lse.data_ptr(),
+                                 B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                 _dtype_code(q.dtype), S, ctypes.c_void_p(s.cuda_stream))
     _check(rc)
     return o, lse

@@ -323,6 +323,38 @@ def test_decode_rejections(kw, code):
     assert decode_call(**kw) == code, kw
 
 
+def decode_noalloc_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN,
+                        lse=BASE + 4 * SPAN, B_=1, Hq=8, Hkv=2, Nq=2, Nk=100, d=128, causal=1,
+                        scale=0.1, dt=F.BF16, S=4):
+    # Invalid arguments only: every call below must be rejected before any HIP call.
+    return F.lib().fa_fwd_decode_noalloc(q, k, v, o, lse, B_, Hq, Hkv, Nq, Nk, d, causal, scale,
+                                         dt, S, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1),
+    (dict(B_=-1), -2), (dict(Nk=0), -2), (dict(Hq=3), -2), (dict(Nq=101), -2),
+    (dict(Nq=9), -3), (dict(d=256), -3), (dict(dt=F.F32, d=64), -3),
+    (dict(S=0), -5), (dict(S=257), -5), (dict(scale=float("inf")), -5),
+    (dict(q=BASE + 8), -4), (dict(lse=BASE + 4 * SPAN + 2), -4), (dict(o=BASE + 64), -5),
+    # The library's workspace holds 16 MiB: 256 pieces of 16 x 8 rows of d = 128 need
+    # 16 MiB of partial outputs plus 128 KiB of partial lse values.
+    (dict(B_=16, Hq=8, Hkv=1, Nq=1, Nk=1 << 16, S=256), -2),
+    (dict(B_=16, Hq=32, Hkv=1, Nq=1, Nk=1 << 16, S=256, d=64, causal=0), -2),
+])
+def test_decode_noalloc_rejections(kw, code):
+    assert decode_noalloc_call(**kw) == code, kw
+
+
+def test_decode_noalloc_workspace_size():
+    assert F.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # 256 pieces x 15 batches x 8 heads: 15 MiB of outputs + 120 KiB of lse fit.
+    assert F.decode_noalloc_bytes(15, 8, 1, 128, 256) == 30720 * 512 + 30720 * 4
+    assert F.decode_noalloc_bytes(15, 8, 1, 128, 256) <= F.NOALLOC_SCRATCH_BYTES
+    assert F.decode_noalloc_bytes(16, 8, 1, 128, 256) > F.NOALLOC_SCRATCH_BYTES
+    assert F.decode_noalloc_bytes(1, 1, 1, 64, 1) == 256 + 4        # lse on a 256-byte boundary
+
+
 def test_decode_allows_more_queries_than_keys_without_causal_mask():
     # Nq > Nk is only an error under the causal mask (checked before any HIP call).
     assert decode_call(Nq=2, Nk=1, S=0, causal=0) == -5
@@ -349,7 +381,10 @@ def test_library_imports_no_allocating_or_copying_call():
         pytest.skip("nm not installed")
     allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipFuncSetAttribute",
-               "hipLaunchKernel"}
+               "hipLaunchKernel",
+               # the static workspace of fa_fwd_decode_noalloc and its per-GPU address
+               "__hipRegisterVar", "hipGetSymbolAddress", "hipStreamGetDevice", "hipGetDevice",
+               "hipSetDevice"}
     for path in (B.LIB_PATH, B.LDS_POISON_LIB_PATH):
         out = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True,
                              check=True).stdout
