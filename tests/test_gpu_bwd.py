@@ -166,6 +166,39 @@ def test_bwd_gqa_equals_repeated_heads():
     assert np.abs(dv - rv).max() <= 1e-5 * np.abs(rv).max()
 
 
+def test_bwd_full_size_two_heads_elementwise():
+    # The headline layer (B1 H32 N4096 d128 causal) in the launch configuration the
+    # benchmark times, with heads 0 and 31 checked element by element against the
+    # fp64 gradient oracle under the bounds of test_bwd_parity.  Heads are
+    # independent (one K/V head per query head), so those two get the oracle's O
+    # (rounded to bf16) and lse; the other 30 take the GPU forward's.
+    x = G.workload("bf16_h32_n4096_d128_causal")
+    assert x.Hq == x.Hkv
+    g = G.make_grad_output(4243, (x.B, x.Hq, x.N, x.d), "bf16")
+    q, k, v = (_dev(getattr(x, n), "bf16") for n in "qkv")
+    o, lse = F.fwd(q, k, v, causal=True, scale=x.scale)
+    heads = (0, x.Hq - 1)
+    one = {}
+    for h in heads:
+        xh = G.AttentionInputs(1, 1, 1, x.N, x.d, "bf16", True, x.scale, x.seed,
+                               x.q[:, h:h + 1], x.k[:, h:h + 1], x.v[:, h:h + 1])
+        dh = G.storage_to_f64(g[:, h:h + 1], "bf16")
+        oh, lh = oracle.attention(xh.f64("q"), xh.f64("k"), xh.f64("v"), True, x.scale)
+        oh_st = G.to_storage(G.round_to_dtype(oh, "bf16"), "bf16")
+        o[:, h:h + 1] = _dev(oh_st, "bf16")
+        lse[:, h:h + 1] = torch.from_numpy(lh.astype(np.float32)).cuda()
+        one[h] = (xh, dh, oh_st)
+    print("bwd full size: B1 H32 N4096 d128 causal, heads", heads, flush=True)
+    dq, dk, dv = F.bwd(q, k, v, o, _dev(g, "bf16"), lse, causal=True, scale=x.scale)
+    torch.cuda.synchronize()
+    for h in heads:
+        xh, dh, oh_st = one[h]
+        rq, rk, rv = oracle.grads(xh.f64("q"), xh.f64("k"), xh.f64("v"), dh, True, x.scale)
+        bq, bk, bv = bounds(xh, dh, oh_st)
+        for name, got, ref, b in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
+            check(f"{name} head {h}", got[:, h:h + 1].cpu().double().numpy(), ref, b)
+
+
 def test_bwd_full_size_invariants():
     # The headline layer (B1 H32 N4096 d128 causal) end to end: forward on the GPU,
     # then backward, in the launch configuration the benchmark times.  A property
