@@ -655,7 +655,7 @@ int run_decode(const void *q, const void *k, const void *v, void *o, float *lse,
         return FA355_ERR_SHAPE;
 
     // Every check has passed: now (and only now) the no-allocation path looks up its
-    // workspace on the current GPU.
+    // workspace on the GPU the stream runs on.
     if (own_scratch) {
         unsigned char *sp = nullptr;
         if (const int e = scratch_for_stream(stream, &sp); e != FA355_OK)

@@ -190,6 +190,9 @@ __device__ __forceinline__ void v_read_offsets(int lane, int (&off)[(D / 32) < 4
         off[q] = base + 64 * (q ^ sw4);
 }
 
+// A compile-time integer as a value (selects unrolled loop bodies).
+template <int V> struct IntC { static constexpr int value = V; };
+
 // Values of lanes L and L^32 (same query row), in a fixed order on both lanes.
 __device__ __forceinline__ f32x2_t row_pair(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -280,7 +283,6 @@ fa_fwd_kernel(FwdArgs a)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
     using M = Mfma<T>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -354,6 +356,12 @@ fa_fwd_kernel(FwdArgs a)
     constexpr int B_CPR = BC / 8;                                   // chunks per row
     constexpr int B_INSTR = BIAS ? Tr::BR * B_CPR / 64 : 0;
     constexpr int STAGE = Tr::STAGE + (BIAS ? Tr::BR * BC * 2 : 0);
+    // The two LDS stages are separate objects, and the loop below is unrolled by two
+    // so that each access names its stage at compile time: the compiler can then
+    // tell that reads of one stage do not alias the buffer-to-LDS copies landing in
+    // the other, and does not make them wait for those copies.
+    __shared__ __attribute__((aligned(16))) char lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) char lds1[STAGE];
     const char *bias_bh = nullptr;
     int bias_bytes = 0;
     if constexpr (BIAS) {
@@ -365,11 +373,10 @@ fa_fwd_kernel(FwdArgs a)
         bias_bytes = (int)((((long long)(N - 1) * a.bias_si + N) * 2 + 3) & ~3LL);
     }
 
-    auto dma_block = [&](int t, int stage) {
+    auto dma_block = [&](int t, char *st) {
         const int j0 = t * BC;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)j0 * ROW, (N - j0) * ROW);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)j0 * ROW, (N - j0) * ROW);
-        char *st = smem + stage * STAGE;
 #pragma unroll
         for (int p = 0; p < Tr::P_INSTR; ++p) {
             const int i = p * WAVES + wave;
@@ -413,21 +420,25 @@ fa_fwd_kernel(FwdArgs a)
 
     if (t_begin < n_kv) {
         if constexpr (kLdsPoison) {
-            lds_poison<Tr::NT>(smem, STAGE, tid);
+            lds_poison<Tr::NT>(lds0, STAGE, tid);
             __syncthreads();
         }
-        dma_block(t_begin, 0);
+        dma_block(t_begin, lds0);
     }
     __syncthreads();
 
-    for (int t = t_begin; t < n_kv; ++t) {
+    // Block t, held in stage S (block t + 1 goes to the other stage).
+    auto iteration = [&](int t, auto stage) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage)::value;
+        char *const cur = S == 0 ? lds0 : lds1;
+        char *const nxt = S == 0 ? lds1 : lds0;
         const int j0 = t * BC;
         if (t + 1 < n_kv) {
             if constexpr (kLdsPoison) {
-                lds_poison<Tr::NT>(smem + ((t + 1 - t_begin) & 1) * STAGE, STAGE, tid);
+                lds_poison<Tr::NT>(nxt, STAGE, tid);
                 __syncthreads();
             }
-            dma_block(t + 1, (t + 1 - t_begin) & 1);
+            dma_block(t + 1, nxt);
             if constexpr (kLdsPoison)
                 __syncthreads();
         }
@@ -436,8 +447,8 @@ fa_fwd_kernel(FwdArgs a)
         // wholly past N, have nothing to add.
         const bool active = iw0 < N && (!CAUSAL || j0 <= iw0 + 31);
         if (active) {
-            const char *kb = smem + ((t - t_begin) & 1) * STAGE + k_rd;
-            const char *vs = smem + ((t - t_begin) & 1) * STAGE + Tr::K_STAGE;
+            const char *kb = cur + k_rd;
+            const char *vs = cur + Tr::K_STAGE;
 
             f32x16_t sacc[Tr::JB];
 #pragma unroll
@@ -467,7 +478,7 @@ fa_fwd_kernel(FwdArgs a)
             if constexpr (BIAS) {
                 // Lane L's keys j0 + 32 jb + 8 g + 4 (L/32) + 0..3 of its row: four
                 // 16-bit values, one 8-byte LDS read.
-                const char *bb = smem + ((t - t_begin) & 1) * STAGE + Tr::STAGE +
+                const char *bb = cur + Tr::STAGE +
                                  (wave * 32 + l32) * BC * 2;
 #pragma unroll
                 for (int jb = 0; jb < Tr::JB; ++jb)
@@ -586,6 +597,11 @@ fa_fwd_kernel(FwdArgs a)
 
         // The barrier's fence also waits for this iteration's DMA.
         __syncthreads();
+    };
+    for (int t = t_begin; t < n_kv; t += 2) {
+        iteration(t, IntC<0>{});
+        if (t + 1 < n_kv)
+            iteration(t + 1, IntC<1>{});
     }
 
     // Epilogue: O = O / l, lse = ln2 * (m + log2 l).

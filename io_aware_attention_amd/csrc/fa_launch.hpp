@@ -10,28 +10,19 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, OUT_F32>;
     const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, OUT_F32>);
-    static const hipError_t attr =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS);
-    if (attr != hipSuccess)
-        return attr;
     FwdArgs arg = a;
     void *params[] = {&arg};
-    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, Tr::LDS, stream);
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, 0, stream);   // static LDS
 }
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
 hipError_t launch_fwd_bias(const FwdArgs &a, hipStream_t stream)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, false>;
-    constexpr int LDS = 2 * (Tr::STAGE + Tr::BR * BC * 2);      // K, V and bias tiles
     const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, false, false, true>);
-    static const hipError_t attr =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (attr != hipSuccess)
-        return attr;
     FwdArgs arg = a;
     void *params[] = {&arg};
-    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, LDS, stream);
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(Tr::NT), params, 0, stream);   // static LDS
 }
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
@@ -39,14 +30,10 @@ hipError_t launch_fwd_split(const FwdArgs &a, hipStream_t stream)
 {
     using Tr = FwdTraits<T, D, BC, WAVES, CAUSAL, false>;
     const void *fn = reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, BC, WAVES, CAUSAL, false, true>);
-    static const hipError_t attr =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS);
-    if (attr != hipSuccess)
-        return attr;
     FwdArgs arg = a;
     void *params[] = {&arg};
     hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles * a.num_splits), dim3(Tr::NT), params,
-                                   Tr::LDS, stream);
+                                   0, stream);   // static LDS
     if (e != hipSuccess)
         return e;
     const int64_t rows = (int64_t)a.B * a.Hq * a.N;
