@@ -13,12 +13,26 @@
 
 namespace fa355 {
 
-// LDS bytes of a 16-bit-input kernel: two stages, each a K block (BC rows of D
-// values plus one 16-byte pad per row, rounded up to whole 1 KB DMA instructions)
-// and an unpadded V block.
+// One K/V stage of a 16-bit-input kernel: a K block (BC rows of D values plus one
+// 16-byte pad per row, rounded up to whole 1 KB DMA instructions) and an unpadded
+// V block.
+constexpr int fwd_stage_bytes(int D, int BC)
+{
+    return 16 * ((BC * (D / 8 + 1) + 63) / 64 * 64 + BC * (D / 8));
+}
+
+// LDS bytes of a 16-bit-input kernel: two stages.
 constexpr int fwd_lds_bytes(int D, int BC)
 {
-    return 2 * 16 * ((BC * (D / 8 + 1) + 63) / 64 * 64 + BC * (D / 8));
+    return 2 * fwd_stage_bytes(D, BC);
+}
+
+// LDS bytes of the head-dim-256 kernel with two wavefronts per SIMD: two stages of
+// 64-key blocks, the P^T operands four pairs exchange (16 KB), the pairs' block
+// maxima and row sums (1 KB each) and the rescale flags.
+constexpr int fwd_pair_lds_bytes()
+{
+    return 2 * fwd_stage_bytes(256, 64) + 4 * 4 * 64 * 16 + 2 * 4 * 2 * 32 * 4 + 16;
 }
 
 struct FwdArgs {
@@ -73,6 +87,11 @@ template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 
 
+// Head dim 256, 128 x 64 tiles, eight wavefronts: pairs of wavefronts share 32
+// query rows (fa_fwd_pair_kernel.hpp).
+template <typename T, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd_pair(const FwdArgs &a, hipStream_t stream);
+
 // Forward with an additive bias on the scaled scores.
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
 hipError_t launch_fwd_bias(const FwdArgs &a, hipStream_t stream);
@@ -118,12 +137,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
     X(T, D, 64, 8, true, false)  X(T, D, 64, 8, true, true)                           \
     X(T, D, 64, 2, false, false) X(T, D, 64, 2, true, false)
 
-// Head dim 256: tiles 128 x 64 and 128 x 32, each also with fp32 output.
+// Head dim 256, one wavefront per 32 rows: tile 128 x 32, also with fp32 output.
+// (The 128 x 64 tile is the wavefront-pair kernel below.)
 #define FA355_VARIANTS_D256(X, T)                                                     \
-    X(T, 256, 64, 4, false, false) X(T, 256, 64, 4, false, true)                      \
-    X(T, 256, 64, 4, true, false)  X(T, 256, 64, 4, true, true)                       \
     X(T, 256, 32, 4, false, false) X(T, 256, 32, 4, false, true)                      \
     X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)
+
+// Head dim 256 with wavefront pairs: P(T, CAUSAL, OUT_F32).
+#define FA355_PAIR_VARIANTS(P, T)                                                     \
+    P(T, false, false) P(T, false, true) P(T, true, false) P(T, true, true)
 
 #define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
 

@@ -260,7 +260,8 @@ struct FwdTraits {
     static constexpr int LDS = 2 * STAGE;
     static_assert(LDS == fwd_lds_bytes(D, BC), "LDS size");
     // Waves per SIMD to fit: two lets one wavefront's softmax run under the other's
-    // matrix work; head dim 256 needs the whole register file for one.  At head dim
+    // matrix work; head dim 256 needs the whole register file for one (the
+    // wavefront-pair kernel, fa_fwd_pair_kernel.hpp, splits that work).  At head dim
     // 64 the fp16 kernel (one row sum) fits four in the register file.
     static constexpr int OCC = (D <= 64 && WAVES == 4 && !Mfma<T>::kRoundedRowSum) ? 4
                              : (D <= 64 || (D == 128 && WAVES >= 4)) ? 2 : 1;

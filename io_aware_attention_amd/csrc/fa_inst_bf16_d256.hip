@@ -2,3 +2,4 @@
 #include "fa_launch.hpp"
 
 FA355_VARIANTS_D256(FA355_INSTANTIATE, BF16)
+FA355_PAIR_VARIANTS(FA355_INSTANTIATE_PAIR, BF16)
