@@ -68,25 +68,91 @@ __device__ __forceinline__ void dma_rows(const char *head, int N, int j0, char *
     }
 }
 
+// A block of 32 rows of a [*, N, D] 16-bit tensor in LDS that is read both along
+// its rows (16-byte fragments: 16 lanes read one chunk of 16 consecutive rows per
+// LDS cycle) and across them (transposed 8-byte reads: 32 lanes read one 64-byte
+// column group of 4 consecutive rows).  Rows are unpadded and chunk c of row r is
+// stored in slot c ^ swz(r): for the row reads swz takes 16 different values over
+// 16 consecutive rows (at D = 64, 8 over the 8 rows of one parity, the other
+// parity using the other half of the banks), and its bits 2 and up send the 4 rows
+// of a transposed read to 4 different 64-byte groups of banks, so neither pattern
+// has bank conflicts.
+template <int D>
+struct SwzBlock {
+    static_assert(D == 64 || D == 128, "head dims of the backward pass");
+    static constexpr int CPR = D / 8;
+    static constexpr int PITCH = D * 2;
+    static constexpr int INSTR = 32 * CPR / 64;
+    static constexpr int BYTES = 32 * PITCH;
+    static __device__ __forceinline__ int swz(int r) {
+        return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+    }
+};
+
+// Rows j0 .. j0+31 into a SwzBlock at `dst` (rows past N read as zero).  Wavefront
+// `wave` of `waves` issues instructions wave, wave + waves, ...
+template <int D>
+__device__ __forceinline__ void dma_rows_swz(const char *head, int N, int j0, char *dst, int wave,
+                                             int waves, int lane)
+{
+    using L = SwzBlock<D>;
+    constexpr int ROW = 2 * D;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(head + (size_t)j0 * ROW, (N - j0) * ROW);
+    for (int i = wave; i < L::INSTR; i += waves) {
+        const int slot = i * 64 + lane;
+        const int row = slot / L::CPR, sl = slot - row * L::CPR;
+        dma16(r, dst + i * 1024, row * ROW + 16 * (sl ^ L::swz(row)));
+    }
+}
+
+// Per-lane byte offsets into a SwzBlock of the 16-byte row fragment (row L % 32,
+// chunks 2 kk + L / 32) for every kk.
+template <int D>
+__device__ __forceinline__ void swz_row_offsets(int lane, int (&off)[D / 16])
+{
+    using L = SwzBlock<D>;
+    const int r = lane & 31, t = (lane >> 5) ^ L::swz(r);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        off[kk] = r * L::PITCH + 16 * ((2 * kk) ^ t);
+}
+
+// Per-lane byte offsets into a SwzBlock of the two transposed 8-byte reads that
+// make up the A operand whose row is column n of 32-column block nb and whose
+// k-slots are rows 16 ks + {0..3, 8..11} + 4 (L/32) -- the order in which
+// pack_rows() lays out the B operand built from an accumulator (see the forward
+// kernel's P.V product): [nb][0] for rows 0..3 (+ 4 (L/32)), [nb][1] for the rows
+// 8 further on; add 16 ks rows.
+template <int D>
+__device__ __forceinline__ void swz_tr_offsets(int lane, int (&off)[D / 32][2])
+{
+    using L = SwzBlock<D>;
+    const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int j = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+        const int row = r + 8 * hi, f = L::swz(row);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+            off[nb][hi] = row * L::PITCH + 16 * ((4 * nb + j) ^ f) + 8 * (lane & 1);
+    }
+}
+
+// The transposed A operand of column block nb, key step ks from a SwzBlock.
+template <int D>
+__device__ __forceinline__ u32x4_t swz_tr_frag(const char *blk, const int (&off)[D / 32][2], int nb, int ks)
+{
+    const char *a = blk + ks * 16 * SwzBlock<D>::PITCH;
+    const u32x2_t lo = read_tr16(a + off[nb][0]), hi = read_tr16(a + off[nb][1]);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // 32 fp32 values (one per row of a block) into LDS at `dst` (1 KB written; lanes
 // past the 8 that carry data, and rows past N, write zeros).
 __device__ __forceinline__ void dma_row_floats(const float *vec, int N, int j0, char *dst, int lane)
 {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vec + j0, (N - j0) * 4);
     dma16(r, dst, lane < 8 ? lane * 16 : 0x7ffffff0);
-}
-
-// Transposed fragment of a row-major 16-bit block at pitch P (bytes): the A operand
-// whose row is column n of 32-column block nb and whose k-slots are rows
-// 16 ks + {0..3, 8..11} + 4 (L/32) -- the order in which pack_rows() lays out the
-// B operand built from an accumulator (see the forward kernel's P.V product).
-template <int P>
-__device__ __forceinline__ u32x4_t tr_frag(const char *blk, int lane, int nb, int ks)
-{
-    const int off = (4 * (lane >> 5) + ((lane & 15) >> 2)) * P + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    const char *a = blk + off + ks * 16 * P + nb * 64;
-    const u32x2_t lo = read_tr16(a), hi = read_tr16(a + 8 * P);
-    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // An accumulator (rows 8*(r/4) + 4*(L/32) + r%4, column L%32) rounded to 16 bits
@@ -149,7 +215,7 @@ struct DkdvTraits {
     static constexpr int BK = 32 * WAVES;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
-    using QL = RowBlock<D, 2>;                 // Q and dO blocks: row and transposed reads
+    using QL = SwzBlock<D>;                    // Q and dO blocks: row and transposed reads
     static constexpr int Q_OFF = 0;
     static constexpr int G_OFF = QL::BYTES;
     static constexpr int L_OFF = 2 * QL::BYTES;        // lse of the block's 32 queries
@@ -217,12 +283,16 @@ fa_bwd_dkdv_kernel(BwdArgs a)
         const size_t bh = (size_t)b * a.Hq + h;
         if (wave < 2) {
             const char *base = static_cast<const char *>(wave == 0 ? a.q : a.dout) + bh * head_bytes;
-            dma_rows<D, 2>(base, N, i0, st + (wave == 0 ? Tr::Q_OFF : Tr::G_OFF), 0, 1, lane);
+            dma_rows_swz<D>(base, N, i0, st + (wave == 0 ? Tr::Q_OFF : Tr::G_OFF), 0, 1, lane);
         } else {
             const float *vec = (wave == 2 ? a.lse : a.delta) + bh * N;
             dma_row_floats(vec, N, i0, st + (wave == 2 ? Tr::L_OFF : Tr::D_OFF), lane);
         }
     };
+
+    int row_off[Tr::DK], tr_off[Tr::NB][2];
+    swz_row_offsets<D>(lane, row_off);
+    swz_tr_offsets<D>(lane, tr_off);
 
     if (steps > 0) {
         if constexpr (kLdsPoison) {
@@ -252,8 +322,8 @@ fa_bwd_dkdv_kernel(BwdArgs a)
             f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
             for (int kk = 0; kk < Tr::DK; ++kk) {
-                const u32x4_t qa = *reinterpret_cast<const u32x4_t *>(qb + l32 * QL::PITCH + kk * 32 + h2 * 16);
-                const u32x4_t ga = *reinterpret_cast<const u32x4_t *>(gb + l32 * QL::PITCH + kk * 32 + h2 * 16);
+                const u32x4_t qa = *reinterpret_cast<const u32x4_t *>(qb + row_off[kk]);
+                const u32x4_t ga = *reinterpret_cast<const u32x4_t *>(gb + row_off[kk]);
                 s = M::run(qa, kf[kk], s);
                 dp = M::run(ga, vf[kk], dp);
             }
@@ -285,8 +355,8 @@ fa_bwd_dkdv_kernel(BwdArgs a)
             for (int nb = 0; nb < Tr::NB; ++nb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    dv[nb] = M::run(tr_frag<QL::PITCH>(gb, lane, nb, ks), pp[ks], dv[nb]);
-                    dk[nb] = M::run(tr_frag<QL::PITCH>(qb, lane, nb, ks), pd[ks], dk[nb]);
+                    dv[nb] = M::run(swz_tr_frag<D>(gb, tr_off, nb, ks), pp[ks], dv[nb]);
+                    dk[nb] = M::run(swz_tr_frag<D>(qb, tr_off, nb, ks), pd[ks], dk[nb]);
                 }
         }
         __syncthreads();      // its fence also waits for the next block's DMA
@@ -324,7 +394,7 @@ struct DqTraits {
     static constexpr int BR = 32 * WAVES;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
-    using KL = RowBlock<D, 2>;                 // K: row reads and transposed reads
+    using KL = SwzBlock<D>;                    // K: row reads and transposed reads
     using VL = RowBlock<D, 1>;                 // V: row reads
     static constexpr int K_OFF = 0;
     static constexpr int V_OFF = KL::BYTES;
@@ -387,10 +457,14 @@ fa_bwd_dq_kernel(BwdArgs a)
     auto load_block = [&](int t, char *st) {
         constexpr int HALF = WAVES / 2;
         if (wave < HALF)
-            dma_rows<D, 2>(kh, N, t * BC, st + Tr::K_OFF, wave, HALF, lane);
+            dma_rows_swz<D>(kh, N, t * BC, st + Tr::K_OFF, wave, HALF, lane);
         else
             dma_rows<D, 1>(vh, N, t * BC, st + Tr::V_OFF, wave - HALF, HALF, lane);
     };
+
+    int row_off[Tr::DK], tr_off[Tr::NB][2];
+    swz_row_offsets<D>(lane, row_off);
+    swz_tr_offsets<D>(lane, tr_off);
 
     if constexpr (kLdsPoison) {
         lds_poison<64 * WAVES>(stage0, Tr::STAGE, tid);
@@ -418,7 +492,7 @@ fa_bwd_dq_kernel(BwdArgs a)
             f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
             for (int kk = 0; kk < Tr::DK; ++kk) {
-                const u32x4_t ka = *reinterpret_cast<const u32x4_t *>(kb + l32 * KL::PITCH + kk * 32 + h2 * 16);
+                const u32x4_t ka = *reinterpret_cast<const u32x4_t *>(kb + row_off[kk]);
                 const u32x4_t va = *reinterpret_cast<const u32x4_t *>(vb + l32 * VL::PITCH + kk * 32 + h2 * 16);
                 s = M::run(ka, qf[kk], s);
                 dp = M::run(va, gf[kk], dp);
@@ -444,7 +518,7 @@ fa_bwd_dq_kernel(BwdArgs a)
             for (int nb = 0; nb < Tr::NB; ++nb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    dq[nb] = M::run(tr_frag<KL::PITCH>(kb, lane, nb, ks), pd[ks], dq[nb]);
+                    dq[nb] = M::run(swz_tr_frag<D>(kb, tr_off, nb, ks), pd[ks], dq[nb]);
         }
         __syncthreads();
     };
