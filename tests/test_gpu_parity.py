@@ -303,6 +303,26 @@ def test_empty_inputs():
                False, "after empty calls")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_growing_row_maximum_d256_pairs(dt, causal):
+    # Head dim 256 (wavefront pairs, 128 x 64 tiles): keys growing along the
+    # sequence drive the rescale path mid-row, and the query rows of one pair
+    # (rows 32..63 of each tile) are scaled up 4x, so in many blocks that pair's
+    # wavefronts go over the cap while the other pairs of the workgroup do not --
+    # the rescale is then taken by some pairs only, with every pair at the barriers.
+    x = G.make_inputs(9450, 1, 2, 2, 700, 256, dt, causal)
+    ramp = 1.0 + np.arange(x.N) / 96.0
+    k = G.to_storage(G.round_to_dtype(x.f64("k") * ramp[:, None], dt), dt)
+    qs = np.ones(x.N)
+    qs[(np.arange(x.N) % 128 >= 32) & (np.arange(x.N) % 128 < 64)] = 4.0
+    q = G.to_storage(G.round_to_dtype(x.f64("q") * qs[:, None], dt), dt)
+    x = G.AttentionInputs(x.B, x.Hq, x.Hkv, x.N, x.d, dt, causal, x.scale, x.seed, q, k, x.v)
+    o_ref, l_ref = full_oracle(x)
+    o, l = run_gpu(x)
+    PT.compare(o, l, o_ref, l_ref, dt, False, f"{dt} d256 pairs growing max causal={causal}")
+
+
 @pytest.mark.parametrize("tl", [None, (128, 32), (64, 64), (256, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_growing_row_maximum(dt, tl):
