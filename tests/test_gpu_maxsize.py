@@ -1,7 +1,8 @@
 """The largest sizes the C ABI accepts, checked through properties with a closed form.
 
 A head's K, V (and Q, O) must fit 32-bit byte offsets: N d 2 <= INT_MAX - 65536 for
-16-bit inputs, i.e. N <= 8,388,351 at d = 128 (a ragged last tile as well).  Inputs
+16-bit inputs, i.e. N <= 8,388,351 at d = 128 and 4,194,175 at d = 256 (the
+wavefront-pair kernel), each with a ragged last tile.  Inputs
 of that size are built on the device, and the expected result comes from integer
 counting rather than from the oracle:
 
@@ -40,13 +41,13 @@ def count_bit(m: np.ndarray, b: int) -> np.ndarray:
     return (m // period) * (1 << b) + np.maximum(0, (m % period) - (1 << b))
 
 
-def expected(m: np.ndarray):
-    """O [len(m), D] and lse [len(m)] for queries that see keys 0 .. m-1."""
+def expected(m: np.ndarray, d: int = D):
+    """O [len(m), d] and lse [len(m)] for queries that see keys 0 .. m-1."""
     M = (m + MARK - 1) // MARK
     U = m - M
     E = math.exp(A)
-    o = np.empty((len(m), D))
-    for c in range(D):
+    o = np.empty((len(m), d))
+    for c in range(d):
         b = c % 24
         call = count_bit(m, b).astype(np.float64)
         cm = count_bit(M, b - 10).astype(np.float64) if b >= 10 else np.zeros(len(m))
@@ -55,34 +56,36 @@ def expected(m: np.ndarray):
     return o, lse
 
 
-def build(n: int, heads: int, dev="cuda"):
+def build(n: int, heads: int, dev="cuda", d: int = D):
     bf = dict(dtype=torch.bfloat16, device=dev)
-    k = torch.zeros(1, heads, n, D, **bf)
+    k = torch.zeros(1, heads, n, d, **bf)
     k[:, :, ::MARK, 0] = A
     j = torch.arange(n, dtype=torch.int32, device=dev)
-    bits = (torch.arange(D, dtype=torch.int32, device=dev) % 24)
-    v = torch.empty(1, heads, n, D, **bf)
+    bits = (torch.arange(d, dtype=torch.int32, device=dev) % 24)
+    v = torch.empty(1, heads, n, d, **bf)
     step = 1 << 20
     for s in range(0, n, step):                 # chunks keep the int32 temporary small
         v[0, :, s:s + step] = ((j[s:s + step, None] >> bits[None, :]) & 1).to(torch.bfloat16)
     return k, v
 
 
-def test_forward_at_largest_n():
+@pytest.mark.parametrize("d", [128, 256])
+def test_forward_at_largest_n(d):
     dev = "cuda"
-    k, v = build(N_MAX, 1)
-    q = torch.zeros(1, 1, N_MAX, D, dtype=torch.bfloat16, device=dev)
+    n_max = (2**31 - 1 - 65536) // (d * 2)
+    k, v = build(n_max, 1, d=d)
+    q = torch.zeros(1, 1, n_max, d, dtype=torch.bfloat16, device=dev)
     q[..., 0] = 1.0
     o, lse = F.fwd(q, k, v, causal=True, scale=1.0)
     torch.cuda.synchronize()
     del q, k, v
-    rows = PT.sample_rows(N_MAX, 256, 9973)
+    rows = PT.sample_rows(n_max, 256 if d == 128 else 128, 9973)
     ri = torch.from_numpy(rows).to(dev)
     og = o[0, 0].index_select(0, ri).float().cpu().double().numpy()
     lg = lse[0, 0].index_select(0, ri).cpu().double().numpy()
-    o_ref, l_ref = expected(rows + 1)
-    stats = PT.compare(og, lg, o_ref, l_ref, "bf16", False, f"N={N_MAX} causal, {len(rows)} rows")
-    print(f"N={N_MAX}: {len(rows)} rows, {stats}", flush=True)
+    o_ref, l_ref = expected(rows + 1, d)
+    stats = PT.compare(og, lg, o_ref, l_ref, "bf16", False, f"N={n_max} d={d} causal, {len(rows)} rows")
+    print(f"N={n_max} d={d}: {len(rows)} rows, {stats}", flush=True)
 
 
 def test_decode_at_largest_cache():
