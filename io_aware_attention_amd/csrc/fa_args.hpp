@@ -29,10 +29,11 @@ constexpr int fwd_lds_bytes(int D, int BC)
 
 // LDS bytes of the head-dim-256 kernel with two wavefronts per SIMD: two stages of
 // 64-key blocks, the P^T operands four pairs exchange (16 KB), the pairs' block
-// maxima and row sums (1 KB each) and the rescale flags.
+// maxima and row sums (1 KB each) and the rescale flags (two block parities x four
+// pairs).
 constexpr int fwd_pair_lds_bytes()
 {
-    return 2 * fwd_stage_bytes(256, 64) + 4 * 4 * 64 * 16 + 2 * 4 * 2 * 32 * 4 + 16;
+    return 2 * fwd_stage_bytes(256, 64) + 4 * 4 * 64 * 16 + 2 * 4 * 2 * 32 * 4 + 2 * 4 * 4;
 }
 
 struct FwdArgs {

@@ -52,7 +52,8 @@ struct PairTraits {
     static constexpr int STAGE = K_STAGE + V_SLOTS * 16;
     static constexpr int PBUF = 4 * 4 * 64 * 16;   // P^T operands: 4 pairs x 4 key steps x 64 lanes
     static constexpr int MBUF = 4 * 2 * 32 * 4;    // one float per (pair, half, row)
-    static constexpr int LDS = 2 * STAGE + PBUF + 2 * MBUF + 16;
+    static constexpr int FLAGS = 2 * 4 * 4;        // rescale flags: [block parity][pair]
+    static constexpr int LDS = 2 * STAGE + PBUF + 2 * MBUF + FLAGS;
     static_assert(STAGE == fwd_stage_bytes(D, BC) && LDS == fwd_pair_lds_bytes(), "LDS size");
 };
 

@@ -67,6 +67,13 @@ def test_valid_call_plans_a_launch():
     assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
     rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
     assert rc == 0 and (p.br, p.bc) == (128, 64)
+    # Head dim 256: eight wavefronts in pairs; two stages, the pairs' P operands
+    # (16 KB), block maxima and row sums (2 x 1 KB), rescale flags (32 B).
+    ceil64 = lambda n: (n + 63) // 64 * 64
+    stage = 16 * (ceil64(64 * 33) + 64 * 32)
+    assert p.waves == 8 and p.lds_bytes == 2 * stage + 16384 + 2048 + 32 == 151584
+    rc, p = check(d=256, N=8192, Hq=8, Hkv=8, tuning=(128, 32))
+    assert rc == 0 and p.waves == 4
     # d = 64: fp16 takes 128 x 32 for short rows, 256 x 64 without a mask from 2048 and
     # 128 x 64 with one from 4096; bf16 takes 256 x 64, except causal rows below 2048.
     f16 = lambda N, c: (check(d=64, N=N, dt=F.F16, causal=c)[1].br, check(d=64, N=N, dt=F.F16, causal=c)[1].bc)
