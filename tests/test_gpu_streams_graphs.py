@@ -6,7 +6,9 @@
 * The forward pass and the decoding pair of kernels are captured into HIP graphs
   (through torch.cuda.CUDAGraph) and replayed several times, with eager work and
   synchronisations between the replays; every replay reproduces the eager result
-  bit for bit.  No library kernel needs a memset, so nothing the capture records
+  bit for bit.  The same holds for the head-dim-256 forward (wavefront pairs), the
+  no-allocation decoding entry point (the caller graph capture is for) and the
+  backward pass.  No library kernel needs a memset, so nothing the capture records
   depends on one.
 """
 import threading
@@ -117,3 +119,56 @@ def test_graph_capture_and_replay():
     o_ref, l_ref = oracle.attention(x.f64("q"), x.f64("k"), x.f64("v"), True, x.scale)
     PT.compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, l_ref,
                "bf16", False, "graph replay")
+
+
+def test_graph_capture_pairs_noalloc_backward():
+    x = G.make_inputs(9980, 1, 4, 2, 333, 256, "bf16", True)
+    q, k, v = PT.to_device(x)
+    dx, dq, dk, dv = _decode_inputs(9981)
+    y = G.make_inputs(9982, 1, 4, 2, 300, 128, "bf16", True)
+    yq, yk, yv = PT.to_device(y)
+    yo, ylse = F.fwd(yq, yk, yv, causal=True, scale=y.scale)
+    g_out = torch.randn(yq.shape, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    od = torch.empty_like(dq)
+    ld = torch.empty(dq.shape[:3], dtype=torch.float32, device="cuda")
+    gq = torch.empty(yq.shape, dtype=torch.float32, device="cuda")
+    gk = torch.empty(yk.shape, dtype=torch.float32, device="cuda")
+    gv = torch.empty(yv.shape, dtype=torch.float32, device="cuda")
+    delta = torch.empty(yq.shape[:3], dtype=torch.float32, device="cuda")
+    outs = (o, lse, od, ld, gq, gk, gv)
+
+    def step(stream):
+        F.fwd(q, k, v, causal=True, scale=x.scale, o=o, lse=lse, stream=stream)
+        F.fwd_decode_noalloc(dq, dk, dv, od, ld, causal=True, scale=dx.scale, stream=stream)
+        F.bwd(yq, yk, yv, yo, g_out, ylse, causal=True, scale=y.scale, dq=gq, dk=gk, dv=gv,
+              delta=delta, stream=stream)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    scratch = torch.empty(1 << 20, device="cuda")
+    for r in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        scratch.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), f"replay {r}, output {i}"
+    import oracle
+    o_ref, l_ref = oracle.attention(x.f64("q"), x.f64("k"), x.f64("v"), True, x.scale)
+    PT.compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, l_ref,
+               "bf16", False, "graph replay, head dim 256")
