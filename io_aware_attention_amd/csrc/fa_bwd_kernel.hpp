@@ -122,7 +122,7 @@ __device__ __forceinline__ void swz_row_offsets(int lane, int (&off)[D / 16])
 // k-slots are rows 16 ks + {0..3, 8..11} + 4 (L/32) -- the order in which
 // pack_rows() lays out the B operand built from an accumulator (see the forward
 // kernel's P.V product): [nb][0] for rows 0..3 (+ 4 (L/32)), [nb][1] for the rows
-// 8 further on; add 16 ks rows.
+// 8 further on; add 16 ks rows (swz(r + 16) = swz(r), so the offsets carry over).
 template <int D>
 __device__ __forceinline__ void swz_tr_offsets(int lane, int (&off)[D / 32][2])
 {
