@@ -449,10 +449,10 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     const int64_t n_tiles = (N + kBwdTile - 1) / kBwdTile;
     if ((int64_t)B * Hq * n_tiles > INT_MAX || (int64_t)B * Hq * N > INT_MAX)
         return FA355_ERR_SHAPE;
-    // delta: 256 / (d / 8) rows per 256-thread workgroup; dK/dV: one 256-thread
+    // delta: 256 / (d / 8) rows per 256-thread workgroup; dK/dV: one 512-thread
     // workgroup per 128 keys; dQ: up to 512 threads per query tile.
     if (!grid_fits(((int64_t)B * Hq * N * (d / 8) + 255) / 256, 256) ||
-        !grid_fits((int64_t)B * Hkv * n_tiles, 256) || !grid_fits((int64_t)B * Hq * n_tiles, 512))
+        !grid_fits((int64_t)B * Hkv * n_tiles, 512) || !grid_fits((int64_t)B * Hq * n_tiles, 512))
         return FA355_ERR_SHAPE;
 
     fa355::BwdArgs a;

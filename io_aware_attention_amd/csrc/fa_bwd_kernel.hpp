@@ -14,11 +14,11 @@
 //
 // Three kernels run in order on one stream:
 //   fa_bwd_delta_kernel  D_i = dO_i . O_i into a caller-owned fp32 buffer;
-//   fa_bwd_dkdv_kernel   one workgroup per (batch, K/V head, 128 keys): each
-//                        wavefront keeps 32 keys' K and V fragments and their dK,
-//                        dV accumulators in registers and walks every query block
-//                        of every query head sharing the K/V head (GQA), so dK and
-//                        dV need no atomics;
+//   fa_bwd_dkdv_role_kernel  one workgroup per (batch, K/V head, 128 keys) that
+//                        walks every query block of every query head sharing the
+//                        K/V head (GQA), so dK and dV need no atomics; two
+//                        wavefronts per SIMD share 32 keys, one keeping K and
+//                        dV in registers, the other V and dK;
 //   fa_bwd_dq_kernel     one workgroup per (batch, query head, 256 or 128 queries):
 //                        each wavefront keeps 32 queries' Q and dO fragments and
 //                        dQ, and walks the key blocks; the wider workgroup shares
@@ -149,10 +149,11 @@ __device__ __forceinline__ u32x4_t swz_tr_frag(const char *blk, const int (&off)
 
 // 32 fp32 values (one per row of a block) into LDS at `dst` (1 KB written; lanes
 // past the 8 that carry data, and rows past N, write zeros).
-__device__ __forceinline__ void dma_row_floats(const float *vec, int N, int j0, char *dst, int lane)
+__device__ __forceinline__ void dma_row_floats(const float *vec, int N, int j0, char *dst, int lane,
+                                               int count = 32)
 {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vec + j0, (N - j0) * 4);
-    dma16(r, dst, lane < 8 ? lane * 16 : 0x7ffffff0);
+    dma16(r, dst, lane < count / 4 ? lane * 16 : 0x7ffffff0);
 }
 
 // An accumulator (rows 8*(r/4) + 4*(L/32) + r%4, column L%32) rounded to 16 bits
@@ -207,38 +208,50 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Workgroup: (batch, K/V head, 128 keys); wavefront: 32 keys.
+// dK, dV with two wavefronts per SIMD by role.  Workgroup: (batch, K/V head, 128
+// keys) of eight wavefronts; wavefronts w and w + 4 (which share a SIMD) own the
+// same 32 keys.  The first computes S = Q K^T and P for each 32-query block,
+// accumulates dV^T += dO^T P and leaves P (fp32) in LDS; the second, one block
+// behind, computes dP = dO V^T, dS = P * (dP - D) and accumulates dK^T += Q^T dS.
+// Q, dO, lse and D blocks go through a ring of three LDS stages (the block being
+// copied, the dV role's and the dK role's), P through three buffers; one barrier
+// per block.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-struct DkdvTraits {
-    static constexpr int WAVES = 4;
-    static constexpr int BK = 32 * WAVES;
+struct DkdvRoleTraits {
+    static constexpr int BK = 128;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
-    using QL = SwzBlock<D>;                    // Q and dO blocks: row and transposed reads
+    using QL = SwzBlock<D>;
     static constexpr int Q_OFF = 0;
     static constexpr int G_OFF = QL::BYTES;
     static constexpr int L_OFF = 2 * QL::BYTES;        // lse of the block's 32 queries
     static constexpr int D_OFF = L_OFF + 1024;         // D of the block's 32 queries
     static constexpr int STAGE = D_OFF + 1024;
+    static constexpr int PBUF = 4 * 64 * 16 * 4;       // P of the four key groups
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-fa_bwd_dkdv_kernel(BwdArgs a)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+fa_bwd_dkdv_role_kernel(BwdArgs a)
 {
-    using Tr = DkdvTraits<T, D, CAUSAL>;
+    using Tr = DkdvRoleTraits<T, D, CAUSAL>;
     using M = Mfma<T>;
-    using QL = typename Tr::QL;
     constexpr int ROW = 2 * D;
     __shared__ __attribute__((aligned(16))) char stage0[Tr::STAGE];
     __shared__ __attribute__((aligned(16))) char stage1[Tr::STAGE];
+    __shared__ __attribute__((aligned(16))) char stage2[Tr::STAGE];
+    __shared__ __attribute__((aligned(16))) char pbuf0[Tr::PBUF];
+    __shared__ __attribute__((aligned(16))) char pbuf1[Tr::PBUF];
+    __shared__ __attribute__((aligned(16))) char pbuf2[Tr::PBUF];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
+    const int kw = wave & 3;                    // the 32 keys this wavefront serves
+    const bool dk_role = wave >= 4;
 
     // Key tile major: every head's first key tile, then every head's second, ...
     // With causal masking the first tiles see the most queries, so the longest
@@ -247,141 +260,169 @@ fa_bwd_dkdv_kernel(BwdArgs a)
     const int bhk = blockIdx.x - kt * (a.B * a.Hkv);
     const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
     const int N = a.N;
-    const int j0w = kt * Tr::BK + wave * 32;   // this wavefront's first key
-    const int jk = j0w + l32;                   // this lane's key (operand column)
+    const int j0w = kt * Tr::BK + kw * 32;
+    const int jk = j0w + l32;
     const int head_bytes = N * ROW;
 
     const char *kh = static_cast<const char *>(a.k) + ((size_t)b * a.Hkv + hk) * head_bytes;
     const char *vh = static_cast<const char *>(a.v) + ((size_t)b * a.Hkv + hk) * head_bytes;
-    u32x4_t kf[Tr::DK], vf[Tr::DK];
-    {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, head_bytes), rv = make_rsrc(vh, head_bytes);
-#pragma unroll
-        for (int kk = 0; kk < Tr::DK; ++kk) {
-            kf[kk] = load16(rk, jk * ROW + (kk * 16 + h2 * 8) * 2) ^ a.q_sign;
-            vf[kk] = load16(rv, jk * ROW + (kk * 16 + h2 * 8) * 2);
-        }
-    }
-
-    f32x16_t dk[Tr::NB], dv[Tr::NB];
-#pragma unroll
-    for (int nb = 0; nb < Tr::NB; ++nb) {
-        dk[nb] = f32x16_t{};
-        dv[nb] = f32x16_t{};
-    }
     const float c = a.c;
-
-    // Query blocks of 32: causal tiles start at the tile's first key.
     const int qb0 = CAUSAL ? (kt * Tr::BK) / 32 : 0;
     const int nqb = (N + 31) / 32;
     const int per_head = nqb - qb0;
     const int steps = per_head * a.group;
 
-    auto load_step = [&](int u, char *st) {
-        const int h = hk * a.group + u / per_head;
-        const int i0 = (qb0 + u % per_head) * 32;
-        const size_t bh = (size_t)b * a.Hq + h;
-        if (wave < 2) {
-            const char *base = static_cast<const char *>(wave == 0 ? a.q : a.dout) + bh * head_bytes;
-            dma_rows_swz<D>(base, N, i0, st + (wave == 0 ? Tr::Q_OFF : Tr::G_OFF), 0, 1, lane);
-        } else {
-            const float *vec = (wave == 2 ? a.lse : a.delta) + bh * N;
-            dma_row_floats(vec, N, i0, st + (wave == 2 ? Tr::L_OFF : Tr::D_OFF), lane);
-        }
-    };
-
     int row_off[Tr::DK], tr_off[Tr::NB][2];
     swz_row_offsets<D>(lane, row_off);
     swz_tr_offsets<D>(lane, tr_off);
 
+    auto stage = [&](auto k) __attribute__((always_inline)) -> char * {
+        constexpr int K = decltype(k)::value;
+        return K == 0 ? stage0 : K == 1 ? stage1 : stage2;
+    };
+    auto pbuf = [&](auto k) __attribute__((always_inline)) -> char * {
+        constexpr int K = decltype(k)::value;
+        return K == 0 ? pbuf0 : K == 1 ? pbuf1 : pbuf2;
+    };
+    auto first_query = [&](int u) { return (qb0 + u % per_head) * 32; };
+    auto load_step = [&](int u, char *st) {
+        const int hq = hk * a.group + u / per_head;
+        const int i0 = first_query(u);
+        const size_t bh = (size_t)b * a.Hq + hq;
+        if (wave < 2) {
+            const char *base = static_cast<const char *>(wave == 0 ? a.q : a.dout) + bh * head_bytes;
+            dma_rows_swz<D>(base, N, i0, st + (wave == 0 ? Tr::Q_OFF : Tr::G_OFF), 0, 1, lane);
+        } else if (wave < 4) {
+            const float *vec = (wave == 2 ? a.lse : a.delta) + bh * N;
+            dma_row_floats(vec, N, i0, st + (wave == 2 ? Tr::L_OFF : Tr::D_OFF), lane);
+        }
+    };
     if (steps > 0) {
         if constexpr (kLdsPoison) {
-            lds_poison<256>(stage0, Tr::STAGE, tid);
+            lds_poison<512>(stage0, Tr::STAGE, tid);
             __syncthreads();
         }
         load_step(0, stage0);
     }
     __syncthreads();
 
-    auto step = [&](auto par, int u) {
-        constexpr int P = decltype(par)::value;
-        const char *st = P == 0 ? stage0 : stage1;
-        if (u + 1 < steps) {
-            if constexpr (kLdsPoison) {
-                lds_poison<256>(P == 0 ? stage1 : stage0, Tr::STAGE, tid);
-                __syncthreads();
-            }
-            load_step(u + 1, P == 0 ? stage1 : stage0);
-            if constexpr (kLdsPoison)
-                __syncthreads();
+    // One role's whole loop and epilogue; the role is a compile-time constant so
+    // each keeps only its own fragments and accumulators live.
+    auto run_role = [&](auto role) __attribute__((always_inline)) {
+        constexpr bool DKR = decltype(role)::value == 1;
+        u32x4_t kv[Tr::DK];                     // K (dV role) or V (dK role) rows
+        {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(DKR ? vh : kh, head_bytes);
+            const uint32_t sign = DKR ? 0u : a.q_sign;
+#pragma unroll
+            for (int kk = 0; kk < Tr::DK; ++kk)
+                kv[kk] = load16(r, jk * ROW + (kk * 16 + h2 * 8) * 2) ^ sign;
         }
-        const int i0 = (qb0 + u % per_head) * 32;
-        if (!CAUSAL || i0 + 31 >= j0w) {
-            const char *qb = st + Tr::Q_OFF, *gb = st + Tr::G_OFF;
-            // S = Q K^T and dP = dO V^T (32 queries x 32 keys): row reads of Q, dO.
-            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+        f32x16_t acc[Tr::NB];
 #pragma unroll
-            for (int kk = 0; kk < Tr::DK; ++kk) {
-                const u32x4_t qa = *reinterpret_cast<const u32x4_t *>(qb + row_off[kk]);
-                const u32x4_t ga = *reinterpret_cast<const u32x4_t *>(gb + row_off[kk]);
-                s = M::run(qa, kf[kk], s);
-                dp = M::run(ga, vf[kk], dp);
-            }
-            // Register r of lane L is query i0 + 8(r/4) + 4 h2 + r%4, key jk.  Only
-            // blocks on the causal diagonal or past N need the visibility test.
-            const bool edge = (CAUSAL && i0 < j0w + 31) || i0 + 32 > N || j0w + 32 > N;
-            float p[16], ds[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4_t lse4 = *reinterpret_cast<const f32x4_t *>(st + Tr::L_OFF + (8 * g + 4 * h2) * 4);
-                const f32x4_t dl4 = *reinterpret_cast<const f32x4_t *>(st + Tr::D_OFF + (8 * g + 4 * h2) * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse4[e] * kLog2e));
-                    if (edge) {
-                        const int qi = i0 + 8 * g + 4 * h2 + e;
-                        const bool vis = qi < N && jk < N && (!CAUSAL || jk <= qi);
-                        p[r] = vis ? p[r] : 0.0f;
-                    }
-                    ds[r] = p[r] * (dp[r] - dl4[e]);
+        for (int nb = 0; nb < Tr::NB; ++nb)
+            acc[nb] = f32x16_t{};
+
+        // Iteration u: copy block u + 1 into stage (u + 1) % 3; the dV role takes
+        // block u (stage and P buffer u % 3), the dK role block u - 1.
+        auto iteration = [&](auto sidx, int u) __attribute__((always_inline)) {
+            constexpr int S = decltype(sidx)::value;
+            constexpr int SN = (S + 1) % 3, SP = (S + 2) % 3;
+            if (u + 1 < steps) {
+                if constexpr (kLdsPoison) {
+                    lds_poison<512>(stage(IntC<SN>{}), Tr::STAGE, tid);
+                    __syncthreads();
                 }
+                load_step(u + 1, stage(IntC<SN>{}));
+                if constexpr (kLdsPoison)
+                    __syncthreads();
             }
-            u32x4_t pp[2], pd[2];
-            pack_rows<T>(p, pp);
-            pack_rows<T>(ds, pd);
-            // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of dO and Q).
+            const int ub = DKR ? u - 1 : u;
+            const bool live = ub >= 0 && ub < steps;
+            const int i0 = live ? first_query(ub) : 0;
+            if (live && (!CAUSAL || i0 + 31 >= j0w)) {
+                const char *st = DKR ? stage(IntC<SP>{}) : stage(IntC<S>{});
+                char *pb = (DKR ? pbuf(IntC<SP>{}) : pbuf(IntC<S>{})) + kw * (Tr::PBUF / 4) + lane * 16;
+                const char *qb = st + Tr::Q_OFF, *gb = st + Tr::G_OFF;
+                // S = Q K^T (dV role) or dP = dO V^T (dK role), 32 queries x 32 keys.
+                f32x16_t s = f32x16_t{};
+                const char *rb = DKR ? gb : qb;
+#pragma unroll
+                for (int kk = 0; kk < Tr::DK; ++kk)
+                    s = M::run(*reinterpret_cast<const u32x4_t *>(rb + row_off[kk]), kv[kk], s);
+                // Register r of lane L is query i0 + 8(r/4) + 4 h2 + r%4, key jk.
+                float x[16];
+                if constexpr (!DKR) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4_t lse4 = *reinterpret_cast<const f32x4_t *>(st + Tr::L_OFF + (8 * g + 4 * h2) * 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lse4[e] * kLog2e));
+                    }
+                    // Only blocks on the causal diagonal or past N need the visibility test.
+                    if ((CAUSAL && i0 < j0w + 31) || i0 + 32 > N || j0w + 32 > N) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int qi = i0 + 8 * (r / 4) + 4 * h2 + r % 4;
+                            const bool vis = qi < N && jk < N && (!CAUSAL || jk <= qi);
+                            x[r] = vis ? x[r] : 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<f32x4_t *>(pb + g * 1024) =
+                            f32x4_t{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4_t p4 = *reinterpret_cast<const f32x4_t *>(pb + g * 1024);
+                        const f32x4_t dl4 = *reinterpret_cast<const f32x4_t *>(st + Tr::D_OFF + (8 * g + 4 * h2) * 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[4 * g + e] = p4[e] * (s[4 * g + e] - dl4[e]);
+                    }
+                }
+                u32x4_t px[2];
+                pack_rows<T>(x, px);
+                // dV^T += dO^T P (transposed dO) or dK^T += Q^T dS (transposed Q).
+                const char *tb = DKR ? qb : gb;
+#pragma unroll
+                for (int nb = 0; nb < Tr::NB; ++nb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        acc[nb] = M::run(swz_tr_frag<D>(tb, tr_off, nb, ks), px[ks], acc[nb]);
+            }
+            // Its fence also waits for the copy of block u + 1 and the P writes.
+            __syncthreads();
+        };
+        for (int u = 0; u <= steps; u += 3) {
+            iteration(IntC<0>{}, u);
+            if (u + 1 <= steps)
+                iteration(IntC<1>{}, u + 1);
+            if (u + 2 <= steps)
+                iteration(IntC<2>{}, u + 2);
+        }
+        // Register r of lane L holds column 8(r/4) + 4 h2 + r%4 of block nb, key jk.
+        if (jk < N) {
+            const size_t row = ((size_t)b * a.Hkv + hk) * N + jk;
+            float *out = DKR ? a.dk : a.dv;
+            const float mul = DKR ? a.scale : 1.0f;
 #pragma unroll
             for (int nb = 0; nb < Tr::NB; ++nb)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    dv[nb] = M::run(swz_tr_frag<D>(gb, tr_off, nb, ks), pp[ks], dv[nb]);
-                    dk[nb] = M::run(swz_tr_frag<D>(qb, tr_off, nb, ks), pd[ks], dk[nb]);
+                for (int g = 0; g < 4; ++g) {
+                    const int n0 = nb * 32 + 8 * g + 4 * h2;
+                    const f32x4_t y = {acc[nb][4 * g] * mul, acc[nb][4 * g + 1] * mul,
+                                       acc[nb][4 * g + 2] * mul, acc[nb][4 * g + 3] * mul};
+                    *reinterpret_cast<f32x4_t *>(out + row * D + n0) = y;
                 }
         }
-        __syncthreads();      // its fence also waits for the next block's DMA
     };
-    for (int u = 0; u < steps; u += 2) {
-        step(Parity<0>{}, u);
-        if (u + 1 < steps)
-            step(Parity<1>{}, u + 1);
-    }
-
-    // Register r of lane L holds column 8(r/4) + 4 h2 + r%4 of block nb, key jk.
-    if (jk < N) {
-        const size_t row = ((size_t)b * a.Hkv + hk) * N + jk;
-#pragma unroll
-        for (int nb = 0; nb < Tr::NB; ++nb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n0 = nb * 32 + 8 * g + 4 * h2;
-                const f32x4_t yk = {dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale,
-                                    dk[nb][4 * g + 2] * a.scale, dk[nb][4 * g + 3] * a.scale};
-                const f32x4_t yv = {dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
-                *reinterpret_cast<f32x4_t *>(a.dk + row * D + n0) = yk;
-                *reinterpret_cast<f32x4_t *>(a.dv + row * D + n0) = yv;
-            }
-    }
+    if (dk_role)
+        run_role(IntC<1>{});
+    else
+        run_role(IntC<0>{});
 }
 
 // ---------------------------------------------------------------------------

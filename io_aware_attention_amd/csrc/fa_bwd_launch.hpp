@@ -16,8 +16,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
                                    dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), params, 0, stream);
     if (e != hipSuccess)
         return e;
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D, CAUSAL>),
-                        dim3(a.B * a.Hkv * a.n_ktiles), dim3(256), params, 0, stream);
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_role_kernel<T, D, CAUSAL>),
+                        dim3(a.B * a.Hkv * a.n_ktiles), dim3(512), params, 0, stream);
     if (e != hipSuccess)
         return e;
     if (a.dq_rows == 256)
