@@ -540,18 +540,23 @@ fa_bwd_dq_kernel(BwdArgs a)
             }
             // Register r of lane L is key j0 + 8(r/4) + 4 h2 + r%4, query iq.  Only
             // blocks on the causal diagonal or past N need the visibility test.
-            const bool edge = (CAUSAL && j0 + 31 > iw0) || j0 + 32 > N;
-            float ds[16];
+            // (One test per block, outside the per-element loop: inside it the
+            // compiler branches once per element.)
+            float p[16], ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-                if (edge) {
+            for (int r = 0; r < 16; ++r)
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+            if ((CAUSAL && j0 + 31 > iw0) || j0 + 32 > N) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
                     const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
                     const bool vis = j < N && (!CAUSAL || j <= iq);
-                    p = vis ? p : 0.0f;
+                    p[r] = vis ? p[r] : 0.0f;
                 }
-                ds[r] = p * (dp[r] - dl);
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ds[r] = p[r] * (dp[r] - dl);
             u32x4_t pd[2];
             pack_rows<T>(ds, pd);
             // dQ^T += K^T dS^T (transposed reads of K).
