@@ -149,11 +149,10 @@ __device__ __forceinline__ u32x4_t swz_tr_frag(const char *blk, const int (&off)
 
 // 32 fp32 values (one per row of a block) into LDS at `dst` (1 KB written; lanes
 // past the 8 that carry data, and rows past N, write zeros).
-__device__ __forceinline__ void dma_row_floats(const float *vec, int N, int j0, char *dst, int lane,
-                                               int count = 32)
+__device__ __forceinline__ void dma_row_floats(const float *vec, int N, int j0, char *dst, int lane)
 {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vec + j0, (N - j0) * 4);
-    dma16(r, dst, lane < count / 4 ? lane * 16 : 0x7ffffff0);
+    dma16(r, dst, lane < 8 ? lane * 16 : 0x7ffffff0);
 }
 
 // An accumulator (rows 8*(r/4) + 4*(L/32) + r%4, column L%32) rounded to 16 bits
