@@ -186,7 +186,7 @@ int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *ls
  *   delta      device pointer [B,Hq,N] fp32, a caller-owned workspace; on return it
  *              holds D_i = dout_i . o_i
  *   B .. scale as for fa_fwd (the same scale and causal flag as the forward call);
- *              dtype F16 or BF16, d in {64, 128}
+ *              dtype F16 or BF16, d in {64, 128, 256}
  * All of q, k, v, o, dout, dq, dk, dv must be 16-byte aligned, lse and delta 4-byte
  * aligned; none of dq, dk, dv, delta may overlap each other or any input.
  * Enqueues three kernels on `stream` and returns; allocates nothing.  Errors as for

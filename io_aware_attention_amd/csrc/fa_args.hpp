@@ -71,7 +71,7 @@ struct BwdArgs {
     int dq_rows;        // queries per dQ workgroup: 128 or 256
     int n_qtiles;       // ceil(N / dq_rows): query tiles of the dQ kernel
     int total_tiles;    // B * Hq * n_qtiles
-    int n_ktiles;       // ceil(N / 128): key tiles of the dK/dV kernel
+    int n_ktiles;       // ceil(N / keys per dK/dV workgroup): 128, or 64 at head dim 256
     float c;            // |scale| * log2(e), FLT_MIN for a zero scale
     float scale;        // the signed scale, applied to dQ and dK
     uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q, or K, in the scores)
@@ -151,7 +151,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 #define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
 
 // Backward variants: Z(T, D, CAUSAL), 16-bit inputs, head dims 64 and 128.
-#define FA355_BWD_VARIANTS(Z, T) Z(T, 64, false) Z(T, 64, true) Z(T, 128, false) Z(T, 128, true)
+#define FA355_BWD_VARIANTS(Z, T) Z(T, 64, false) Z(T, 64, true) Z(T, 128, false) Z(T, 128, true) \
+    Z(T, 256, false) Z(T, 256, true)
 
 // Split-KV variants: S(T, D, BC, WAVES, CAUSAL): 64-key blocks, 128-row tiles at
 // head dim 64 and 256-row tiles at 128.

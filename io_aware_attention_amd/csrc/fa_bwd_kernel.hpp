@@ -76,10 +76,11 @@ __device__ __forceinline__ void dma_rows(const char *head, int N, int j0, char *
 // 16 consecutive rows (at D = 64, 8 over the 8 rows of one parity, the other
 // parity using the other half of the banks), and its bits 2 and up send the 4 rows
 // of a transposed read to 4 different 64-byte groups of banks, so neither pattern
-// has bank conflicts.
+// has bank conflicts.  Rows of 256 and 512 bytes (D = 128, 256) start on the same
+// bank, so both take the same swz.
 template <int D>
 struct SwzBlock {
-    static_assert(D == 64 || D == 128, "head dims of the backward pass");
+    static_assert(D == 64 || D == 128 || D == 256, "head dims of the backward pass");
     static constexpr int CPR = D / 8;
     static constexpr int PITCH = D * 2;
     static constexpr int INSTR = 32 * CPR / 64;
@@ -207,18 +208,24 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV with two wavefronts per SIMD by role.  Workgroup: (batch, K/V head, 128
-// keys) of eight wavefronts; wavefronts w and w + 4 (which share a SIMD) own the
-// same 32 keys.  The first computes S = Q K^T and P for each 32-query block,
-// accumulates dV^T += dO^T P and leaves P (fp32) in LDS; the second, one block
-// behind, computes dP = dO V^T, dS = P * (dP - D) and accumulates dK^T += Q^T dS.
-// Q, dO, lse and D blocks go through a ring of three LDS stages (the block being
-// copied, the dV role's and the dK role's), P through three buffers; one barrier
-// per block.
+// dK, dV with the wavefronts in two roles.  Workgroup: (batch, K/V head, 32 PAIRS
+// keys) of 2 PAIRS wavefronts; wavefronts w and w + PAIRS own the same 32 keys.  The
+// first computes S = Q K^T and P for each 32-query block, accumulates dV^T += dO^T P
+// and leaves P (fp32) in LDS; the second, one block behind, computes dP = dO V^T,
+// dS = P * (dP - D) and accumulates dK^T += Q^T dS.  Q, dO, lse and D blocks go
+// through a ring of three LDS stages (the block being copied, the dV role's and the
+// dK role's), P through three buffers; one barrier per block.  At head dims 64 and
+// 128 there are four pairs, and the two wavefronts of a pair share a SIMD; at 256
+// each wavefront needs more than half a SIMD's register file, so two pairs run with
+// one wavefront per SIMD.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int dkdv_pairs() { return D == 256 ? 2 : 4; }
+
 template <typename T, int D, bool CAUSAL>
 struct DkdvRoleTraits {
-    static constexpr int BK = 128;
+    static constexpr int PAIRS = dkdv_pairs<D>();
+    static constexpr int BK = 32 * PAIRS;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
     using QL = SwzBlock<D>;
@@ -227,11 +234,12 @@ struct DkdvRoleTraits {
     static constexpr int L_OFF = 2 * QL::BYTES;        // lse of the block's 32 queries
     static constexpr int D_OFF = L_OFF + 1024;         // D of the block's 32 queries
     static constexpr int STAGE = D_OFF + 1024;
-    static constexpr int PBUF = 4 * 64 * 16 * 4;       // P of the four key groups
+    static constexpr int PBUF = PAIRS * 64 * 16 * 4;   // P of the key groups
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(128 * dkdv_pairs<D>())
+__attribute__((amdgpu_waves_per_eu(dkdv_pairs<D>() == 4 ? 2 : 1)))
 fa_bwd_dkdv_role_kernel(BwdArgs a)
 {
     using Tr = DkdvRoleTraits<T, D, CAUSAL>;
@@ -249,8 +257,8 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
-    const int kw = wave & 3;                    // the 32 keys this wavefront serves
-    const bool dk_role = wave >= 4;
+    const int kw = wave & (Tr::PAIRS - 1);      // the 32 keys this wavefront serves
+    const bool dk_role = wave >= Tr::PAIRS;
 
     // Key tile major: every head's first key tile, then every head's second, ...
     // With causal masking the first tiles see the most queries, so the longest
@@ -298,7 +306,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
     };
     if (steps > 0) {
         if constexpr (kLdsPoison) {
-            lds_poison<512>(stage0, Tr::STAGE, tid);
+            lds_poison<128 * Tr::PAIRS>(stage0, Tr::STAGE, tid);
             __syncthreads();
         }
         load_step(0, stage0);
@@ -329,7 +337,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
             constexpr int SN = (S + 1) % 3, SP = (S + 2) % 3;
             if (u + 1 < steps) {
                 if constexpr (kLdsPoison) {
-                    lds_poison<512>(stage(IntC<SN>{}), Tr::STAGE, tid);
+                    lds_poison<128 * Tr::PAIRS>(stage(IntC<SN>{}), Tr::STAGE, tid);
                     __syncthreads();
                 }
                 load_step(u + 1, stage(IntC<SN>{}));
@@ -341,7 +349,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
             const int i0 = live ? first_query(ub) : 0;
             if (live && (!CAUSAL || i0 + 31 >= j0w)) {
                 const char *st = DKR ? stage(IntC<SP>{}) : stage(IntC<S>{});
-                char *pb = (DKR ? pbuf(IntC<SP>{}) : pbuf(IntC<S>{})) + kw * (Tr::PBUF / 4) + lane * 16;
+                char *pb = (DKR ? pbuf(IntC<SP>{}) : pbuf(IntC<S>{})) + kw * 4096 + lane * 16;
                 const char *qb = st + Tr::Q_OFF, *gb = st + Tr::G_OFF;
                 // S = Q K^T (dV role) or dP = dO V^T (dK role), 32 queries x 32 keys.
                 f32x16_t s = f32x16_t{};
@@ -442,7 +450,7 @@ struct DqTraits {
 };
 
 template <typename T, int D, bool CAUSAL, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 fa_bwd_dq_kernel(BwdArgs a)
 {
     using Tr = DqTraits<T, D, CAUSAL, WAVES>;

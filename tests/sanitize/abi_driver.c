@@ -66,7 +66,7 @@ int main(void)
            FA355_ERR_UNSUPPORTED);
     EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), F(6), F(7), F(8), F(9), NULL, 1, 4, 2, 100, 128, 1, 0.1f,
                   FA355_BF16, NULL), FA355_ERR_NULL);
-    EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), F(6), F(7), F(8), F(9), F(10), 1, 4, 2, 100, 256, 1, 0.1f,
+    EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), F(6), F(7), F(8), F(9), F(10), 1, 4, 2, 100, 32, 1, 0.1f,
                   FA355_BF16, NULL), FA355_ERR_UNSUPPORTED);
     EXPECT(fa_fwd_split(P(1), P(2), P(3), P(4), F(5), 1, 4, 2, 100, 128, 1, 0.1f, FA355_BF16, 17, F(6), F(7), NULL),
            FA355_ERR_ARG);

@@ -232,7 +232,7 @@ def bwd_call(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, do=BAS
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(do=None), -1), (dict(lse=None), -1), (dict(delta=None), -1),
     (dict(dq=None), -1), (dict(B_=-1), -2), (dict(Hq=3, Hkv=2), -2), (dict(N=-1), -2),
-    (dict(d=256), -3), (dict(d=96), -3), (dict(dt=F.F32, d=64), -3), (dict(dt=9), -3),
+    (dict(d=32), -3), (dict(d=96), -3), (dict(dt=F.F32, d=64), -3), (dict(dt=9), -3),
     (dict(scale=float("nan")), -5), (dict(q=BASE + 8), -4), (dict(dk=BASE + 7 * SPAN + 4), -4),
     (dict(lse=BASE + 5 * SPAN + 2), -4), (dict(dq=BASE), -5), (dict(dv=BASE + 7 * SPAN + 64), -5),
     (dict(delta=BASE + 4 * SPAN + 128), -5), (dict(dk=BASE + 6 * SPAN + 4096), -5),

@@ -109,6 +109,11 @@ CASES = [
     # with a ragged last tile.
     (8, 16, 4, 300, 128, "bf16", True, 1.0, None),
     (16, 16, 16, 260, 64, "f16", False, 1.0, None),
+    # Head dim 256: two wavefront pairs per dK/dV workgroup (64 keys), one wavefront
+    # per SIMD; 128-query dQ workgroups.
+    (1, 2, 2, 200, 256, "bf16", True, 1.0, None),
+    (1, 4, 2, 130, 256, "f16", False, 1.0, None),
+    (1, 2, 1, 97, 256, "bf16", True, 2.0, -0.3),
 ]
 
 

@@ -113,6 +113,7 @@ def test_decode(causal):
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,dt,causal", [
     (1, 4, 2, 300, 128, "bf16", True),
     (2, 2, 2, 77, 64, "f16", False),
+    (1, 2, 1, 150, 256, "bf16", True),
 ])
 def test_backward(B, Hq, Hkv, N, d, dt, causal):
     x = G.make_inputs(9920 + N, B, Hq, Hkv, N, d, dt, causal)
