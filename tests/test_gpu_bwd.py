@@ -114,6 +114,7 @@ CASES = [
     (1, 2, 2, 200, 256, "bf16", True, 1.0, None),
     (1, 4, 2, 130, 256, "f16", False, 1.0, None),
     (1, 2, 1, 97, 256, "bf16", True, 2.0, -0.3),
+    (1, 2, 2, 1024, 256, "bf16", True, 3.0, None),
 ]
 
 
@@ -204,13 +205,15 @@ def test_bwd_full_size_two_heads_elementwise():
             check(f"{name} head {h}", got[:, h:h + 1].cpu().double().numpy(), ref, b)
 
 
-def test_bwd_full_size_invariants():
-    # The headline layer (B1 H32 N4096 d128 causal) end to end: forward on the GPU,
-    # then backward, in the launch configuration the benchmark times.  A property
-    # that holds at any size: sum_j dV_j = sum_i (sum_j P_ij) dO_i = sum_i dO_i,
-    # up to the rounding of P to bf16 (u = 2^-8 relative) and the forward lse's
-    # error (< 1e-3): |sum_j dV_jt - sum_i dO_it| <= 2 (u + 1e-3) sum_i |dO_it|.
-    x = G.workload("bf16_h32_n4096_d128_causal")
+@pytest.mark.parametrize("name", ["bf16_h32_n4096_d128_causal", "bf16_h8_n8192_d256_causal_x3"])
+def test_bwd_full_size_invariants(name):
+    # The headline layer (B1 H32 N4096 d128 causal) and the head-dim-256 layer (B1 H8
+    # N8192 causal, inputs x3) end to end: forward on the GPU, then backward, in the
+    # launch configuration the benchmark times.  A property that holds at any size:
+    # sum_j dV_j = sum_i (sum_j P_ij) dO_i = sum_i dO_i, up to the rounding of P to
+    # bf16 (u = 2^-8 relative) and the forward lse's error (< 1e-3):
+    # |sum_j dV_jt - sum_i dO_it| <= 2 (u + 1e-3) sum_i |dO_it|.
+    x = G.workload(name)
     g = G.make_grad_output(4242, (x.B, x.Hq, x.N, x.d), "bf16")
     q, k, v = (_dev(getattr(x, n), "bf16") for n in "qkv")
     o, lse = F.fwd(q, k, v, causal=True, scale=x.scale)
