@@ -447,16 +447,12 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     if (!var)
         return FA355_ERR_UNSUPPORTED;
     const int64_t n_tiles = (N + kBwdTile - 1) / kBwdTile;
-    // Keys per dK/dV workgroup: 128 (four wavefront pairs), 64 at head dim 256 (two).
-    const int kkeys = d == 256 ? kBwdTile / 2 : kBwdTile;
-    const int64_t n_ktiles = (N + kkeys - 1) / kkeys;
-    if ((int64_t)B * Hkv * n_ktiles > INT_MAX || (int64_t)B * Hq * n_tiles > INT_MAX ||
-        (int64_t)B * Hq * N > INT_MAX)
+    if ((int64_t)B * Hq * n_tiles > INT_MAX || (int64_t)B * Hq * N > INT_MAX)
         return FA355_ERR_SHAPE;
-    // delta: 256 / (d / 8) rows per 256-thread workgroup; dK/dV: one workgroup of up
-    // to 512 threads per 128 keys; dQ: up to 512 threads per query tile.
+    // delta: 256 / (d / 8) rows per 256-thread workgroup; dK/dV: one 512-thread
+    // workgroup per 128 keys; dQ: up to 512 threads per query tile.
     if (!grid_fits(((int64_t)B * Hq * N * (d / 8) + 255) / 256, 256) ||
-        !grid_fits((int64_t)B * Hkv * n_ktiles, 512) || !grid_fits((int64_t)B * Hq * n_tiles, 512))
+        !grid_fits((int64_t)B * Hkv * n_tiles, 512) || !grid_fits((int64_t)B * Hq * n_tiles, 512))
         return FA355_ERR_SHAPE;
 
     fa355::BwdArgs a;
@@ -482,7 +478,7 @@ int run_bwd(const void *q, const void *k, const void *v, const void *o, const vo
     a.dq_rows = d != 256 && (int64_t)B * Hq * wide >= kBwdCus ? kBwdTileWide : kBwdTile;
     a.n_qtiles = (int)(a.dq_rows == kBwdTileWide ? wide : n_tiles);
     a.total_tiles = (int)(B * Hq * a.n_qtiles);
-    a.n_ktiles = (int)n_ktiles;
+    a.n_ktiles = (int)n_tiles;
     float c = (float)(std::fabs((double)scale) * 1.4426950408889634);
     if (!(c >= 1.17549435e-38f))
         c = 1.17549435e-38f;

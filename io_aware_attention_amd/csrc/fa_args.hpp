@@ -71,7 +71,7 @@ struct BwdArgs {
     int dq_rows;        // queries per dQ workgroup: 128 or 256
     int n_qtiles;       // ceil(N / dq_rows): query tiles of the dQ kernel
     int total_tiles;    // B * Hq * n_qtiles
-    int n_ktiles;       // ceil(N / keys per dK/dV workgroup): 128, or 64 at head dim 256
+    int n_ktiles;       // ceil(N / 128): key tiles of the dK/dV kernel
     float c;            // |scale| * log2(e), FLT_MIN for a zero scale
     float scale;        // the signed scale, applied to dQ and dK
     uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q, or K, in the scores)

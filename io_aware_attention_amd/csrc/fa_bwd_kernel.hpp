@@ -107,15 +107,24 @@ __device__ __forceinline__ void dma_rows_swz(const char *head, int N, int j0, ch
 }
 
 // Per-lane byte offsets into a SwzBlock of the 16-byte row fragment (row L % 32,
-// chunks 2 kk + L / 32) for every kk.
+// chunks 2 kk + L / 32): slot kk & 7, plus 256 bytes per 8 kk (the swizzle only
+// permutes chunks within each 256-byte half of a 512-byte row), so head dim 256
+// needs eight offsets, not sixteen.
 template <int D>
-__device__ __forceinline__ void swz_row_offsets(int lane, int (&off)[D / 16])
+constexpr int swz_row_slots() { return D / 16 < 8 ? D / 16 : 8; }
+template <int D>
+__device__ __forceinline__ void swz_row_offsets(int lane, int (&off)[swz_row_slots<D>()])
 {
     using L = SwzBlock<D>;
     const int r = lane & 31, t = (lane >> 5) ^ L::swz(r);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < swz_row_slots<D>(); ++kk)
         off[kk] = r * L::PITCH + 16 * ((2 * kk) ^ t);
+}
+template <int D>
+__device__ __forceinline__ int swz_row_at(const int (&off)[swz_row_slots<D>()], int kk)
+{
+    return off[kk & 7] + 256 * (kk >> 3);
 }
 
 // Per-lane byte offsets into a SwzBlock of the two transposed 8-byte reads that
@@ -124,8 +133,11 @@ __device__ __forceinline__ void swz_row_offsets(int lane, int (&off)[D / 16])
 // pack_rows() lays out the B operand built from an accumulator (see the forward
 // kernel's P.V product): [nb][0] for rows 0..3 (+ 4 (L/32)), [nb][1] for the rows
 // 8 further on; add 16 ks rows (swz(r + 16) = swz(r), so the offsets carry over).
+// Slot nb & 3, plus 256 bytes per 4 nb (as for the row reads).
 template <int D>
-__device__ __forceinline__ void swz_tr_offsets(int lane, int (&off)[D / 32][2])
+constexpr int swz_tr_slots() { return D / 32 < 4 ? D / 32 : 4; }
+template <int D>
+__device__ __forceinline__ void swz_tr_offsets(int lane, int (&off)[swz_tr_slots<D>()][2])
 {
     using L = SwzBlock<D>;
     const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
@@ -134,17 +146,17 @@ __device__ __forceinline__ void swz_tr_offsets(int lane, int (&off)[D / 32][2])
     for (int hi = 0; hi < 2; ++hi) {
         const int row = r + 8 * hi, f = L::swz(row);
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb)
+        for (int nb = 0; nb < swz_tr_slots<D>(); ++nb)
             off[nb][hi] = row * L::PITCH + 16 * ((4 * nb + j) ^ f) + 8 * (lane & 1);
     }
 }
 
 // The transposed A operand of column block nb, key step ks from a SwzBlock.
 template <int D>
-__device__ __forceinline__ u32x4_t swz_tr_frag(const char *blk, const int (&off)[D / 32][2], int nb, int ks)
+__device__ __forceinline__ u32x4_t swz_tr_frag(const char *blk, const int (&off)[swz_tr_slots<D>()][2], int nb, int ks)
 {
-    const char *a = blk + ks * 16 * SwzBlock<D>::PITCH;
-    const u32x2_t lo = read_tr16(a + off[nb][0]), hi = read_tr16(a + off[nb][1]);
+    const char *a = blk + ks * 16 * SwzBlock<D>::PITCH + 256 * (nb >> 2);
+    const u32x2_t lo = read_tr16(a + off[nb & 3][0]), hi = read_tr16(a + off[nb & 3][1]);
     return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -208,24 +220,20 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV with the wavefronts in two roles.  Workgroup: (batch, K/V head, 32 PAIRS
-// keys) of 2 PAIRS wavefronts; wavefronts w and w + PAIRS own the same 32 keys.  The
-// first computes S = Q K^T and P for each 32-query block, accumulates dV^T += dO^T P
-// and leaves P (fp32) in LDS; the second, one block behind, computes dP = dO V^T,
-// dS = P * (dP - D) and accumulates dK^T += Q^T dS.  Q, dO, lse and D blocks go
-// through a ring of three LDS stages (the block being copied, the dV role's and the
-// dK role's), P through three buffers; one barrier per block.  At head dims 64 and
-// 128 there are four pairs, and the two wavefronts of a pair share a SIMD; at 256
-// each wavefront needs more than half a SIMD's register file, so two pairs run with
-// one wavefront per SIMD.
+// dK, dV with two wavefronts per SIMD by role.  Workgroup: (batch, K/V head, 128
+// keys) of eight wavefronts; wavefronts w and w + 4 (which share a SIMD) own the
+// same 32 keys.  The first computes S = Q K^T and P for each 32-query block,
+// accumulates dV^T += dO^T P and leaves P (fp32) in LDS; the second, one block
+// behind, computes dP = dO V^T, dS = P * (dP - D) and accumulates dK^T += Q^T dS.
+// Q, dO, lse and D blocks go through a ring of three LDS stages (the block being
+// copied, the dV role's and the dK role's), P through three buffers; one barrier
+// per block.  (At head dim 256 each role's fragments and accumulator slightly
+// exceed half a SIMD's register file and some registers spill; two wavefronts per
+// SIMD still beat one by 16 %.)
 // ---------------------------------------------------------------------------
-template <int D>
-constexpr int dkdv_pairs() { return D == 256 ? 2 : 4; }
-
 template <typename T, int D, bool CAUSAL>
 struct DkdvRoleTraits {
-    static constexpr int PAIRS = dkdv_pairs<D>();
-    static constexpr int BK = 32 * PAIRS;
+    static constexpr int BK = 128;
     static constexpr int DK = D / 16;
     static constexpr int NB = D / 32;
     using QL = SwzBlock<D>;
@@ -234,12 +242,11 @@ struct DkdvRoleTraits {
     static constexpr int L_OFF = 2 * QL::BYTES;        // lse of the block's 32 queries
     static constexpr int D_OFF = L_OFF + 1024;         // D of the block's 32 queries
     static constexpr int STAGE = D_OFF + 1024;
-    static constexpr int PBUF = PAIRS * 64 * 16 * 4;   // P of the key groups
+    static constexpr int PBUF = 4 * 64 * 16 * 4;       // P of the four key groups
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(128 * dkdv_pairs<D>())
-__attribute__((amdgpu_waves_per_eu(dkdv_pairs<D>() == 4 ? 2 : 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 fa_bwd_dkdv_role_kernel(BwdArgs a)
 {
     using Tr = DkdvRoleTraits<T, D, CAUSAL>;
@@ -257,8 +264,8 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
-    const int kw = wave & (Tr::PAIRS - 1);      // the 32 keys this wavefront serves
-    const bool dk_role = wave >= Tr::PAIRS;
+    const int kw = wave & 3;                    // the 32 keys this wavefront serves
+    const bool dk_role = wave >= 4;
 
     // Key tile major: every head's first key tile, then every head's second, ...
     // With causal masking the first tiles see the most queries, so the longest
@@ -279,7 +286,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
     const int per_head = nqb - qb0;
     const int steps = per_head * a.group;
 
-    int row_off[Tr::DK], tr_off[Tr::NB][2];
+    int row_off[swz_row_slots<D>()], tr_off[swz_tr_slots<D>()][2];
     swz_row_offsets<D>(lane, row_off);
     swz_tr_offsets<D>(lane, tr_off);
 
@@ -306,7 +313,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
     };
     if (steps > 0) {
         if constexpr (kLdsPoison) {
-            lds_poison<128 * Tr::PAIRS>(stage0, Tr::STAGE, tid);
+            lds_poison<512>(stage0, Tr::STAGE, tid);
             __syncthreads();
         }
         load_step(0, stage0);
@@ -337,7 +344,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
             constexpr int SN = (S + 1) % 3, SP = (S + 2) % 3;
             if (u + 1 < steps) {
                 if constexpr (kLdsPoison) {
-                    lds_poison<128 * Tr::PAIRS>(stage(IntC<SN>{}), Tr::STAGE, tid);
+                    lds_poison<512>(stage(IntC<SN>{}), Tr::STAGE, tid);
                     __syncthreads();
                 }
                 load_step(u + 1, stage(IntC<SN>{}));
@@ -356,7 +363,7 @@ fa_bwd_dkdv_role_kernel(BwdArgs a)
                 const char *rb = DKR ? gb : qb;
 #pragma unroll
                 for (int kk = 0; kk < Tr::DK; ++kk)
-                    s = M::run(*reinterpret_cast<const u32x4_t *>(rb + row_off[kk]), kv[kk], s);
+                    s = M::run(*reinterpret_cast<const u32x4_t *>(rb + swz_row_at<D>(row_off, kk)), kv[kk], s);
                 // Register r of lane L is query i0 + 8(r/4) + 4 h2 + r%4, key jk.
                 float x[16];
                 if constexpr (!DKR) {
@@ -510,7 +517,7 @@ fa_bwd_dq_kernel(BwdArgs a)
             dma_rows<D, 1>(vh, N, t * BC, st + Tr::V_OFF, wave - HALF, HALF, lane);
     };
 
-    int row_off[Tr::DK], tr_off[Tr::NB][2];
+    int row_off[swz_row_slots<D>()], tr_off[swz_tr_slots<D>()][2];
     swz_row_offsets<D>(lane, row_off);
     swz_tr_offsets<D>(lane, tr_off);
 
@@ -540,7 +547,7 @@ fa_bwd_dq_kernel(BwdArgs a)
             f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
             for (int kk = 0; kk < Tr::DK; ++kk) {
-                const u32x4_t ka = *reinterpret_cast<const u32x4_t *>(kb + row_off[kk]);
+                const u32x4_t ka = *reinterpret_cast<const u32x4_t *>(kb + swz_row_at<D>(row_off, kk));
                 const u32x4_t va = *reinterpret_cast<const u32x4_t *>(vb + l32 * VL::PITCH + kk * 32 + h2 * 16);
                 s = M::run(ka, qf[kk], s);
                 dp = M::run(va, gf[kk], dp);

@@ -17,7 +17,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_role_kernel<T, D, CAUSAL>),
-                        dim3(a.B * a.Hkv * a.n_ktiles), dim3(128 * dkdv_pairs<D>()), params, 0, stream);
+                        dim3(a.B * a.Hkv * a.n_ktiles), dim3(512), params, 0, stream);
     if (e != hipSuccess)
         return e;
     if constexpr (D != 256) {
