@@ -189,8 +189,10 @@ int fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *ls
  *              dtype F16 or BF16, d in {64, 128, 256}
  * All of q, k, v, o, dout, dq, dk, dv must be 16-byte aligned, lse and delta 4-byte
  * aligned; none of dq, dk, dv, delta may overlap each other or any input.
- * Enqueues three kernels on `stream` and returns; allocates nothing.  Errors as for
- * fa_fwd: validation runs before any HIP call and leaves the outputs untouched.
+ * Enqueues three kernels on `stream` and returns; allocates nothing (at d = 256 the
+ * dK/dV kernel keeps a few registers in the per-lane private memory the HIP runtime
+ * provides for every kernel).  Errors as for fa_fwd: validation runs before any HIP
+ * call and leaves the outputs untouched.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, float *dq, float *dk, float *dv, float *delta,
