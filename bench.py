@@ -134,11 +134,12 @@ def kernel_code_hashes(lib_path: str) -> dict:
 
 def fwd_kernel_symbol(dtype: str, d: int, bc: int, waves: int, causal: bool) -> str:
     """Mangled name of the forward kernel a plan launches (output in the input type,
-    no split, no bias).  Head dim 256 with eight wavefronts is the wavefront-pair
-    kernel."""
+    no split, no bias).  Head dim 256 with eight wavefronts is the kernel split by
+    role (32-key blocks) or the wavefront-pair kernel (64-key blocks)."""
     t = {"bf16": "4BF16", "f16": "3F16"}[dtype]
     if d == 256 and waves == 8:
-        return f"_ZN5fa35518fa_fwd_pair_kernelINS_{t}ELb{int(causal)}ELb0EEEvNS_7FwdArgsE"
+        kind = "18fa_fwd_role_kernel" if bc == 32 else "18fa_fwd_pair_kernel"
+        return f"_ZN5fa355{kind}INS_{t}ELb{int(causal)}ELb0EEEvNS_7FwdArgsE"
     return (f"_ZN5fa35513fa_fwd_kernelINS_{t}ELi{d}ELi{bc}ELi{waves}ELb{int(causal)}"
             f"ELb0ELb0ELb0EEEvNS_7FwdArgsE")
 

@@ -39,18 +39,20 @@ struct Variant {
     {FA355_DT_##T, D, BC, W, C, O, 32 * W, fa355::fwd_lds_bytes(D, BC), &fa355::launch_fwd<fa355::T, D, BC, W, C, O>},
 #define FA355_ROW_PAIR(T, C, O) \
     {FA355_DT_##T, 256, 64, 8, C, O, 128, fa355::fwd_pair_lds_bytes(), &fa355::launch_fwd_pair<fa355::T, C, O>},
+#define FA355_ROW_ROLE(T, C, O) \
+    {FA355_DT_##T, 256, 32, 8, C, O, 128, fa355::fwd_role_lds_bytes(), &fa355::launch_fwd_role<fa355::T, C, O>},
 #define FA355_ROW_F32(W, C) \
     {FA355_F32, 64, 32, W, C, false, 32 * W, (32 * 65 + 32 * 64) * 4, &fa355::launch_fwd_f32<W, C>},
 
 const Variant kVariants[] = {
     FA355_VARIANTS_D64_D128(FA355_ROW, BF16, 64)
     FA355_VARIANTS_D64_D128(FA355_ROW, BF16, 128)
+    FA355_ROLE_VARIANTS(FA355_ROW_ROLE, BF16)
     FA355_PAIR_VARIANTS(FA355_ROW_PAIR, BF16)
-    FA355_VARIANTS_D256(FA355_ROW, BF16)
     FA355_VARIANTS_D64_D128(FA355_ROW, F16, 64)
     FA355_VARIANTS_D64_D128(FA355_ROW, F16, 128)
+    FA355_ROLE_VARIANTS(FA355_ROW_ROLE, F16)
     FA355_PAIR_VARIANTS(FA355_ROW_PAIR, F16)
-    FA355_VARIANTS_D256(FA355_ROW, F16)
     FA355_VARIANTS_F32(FA355_ROW_F32)
 };
 
@@ -78,10 +80,12 @@ void default_tile(int dt, int d, int N, bool causal, int &br, int &bc)
         br = 32;
         bc = 32;
     } else if (d == 256) {
-        // Wavefront pairs (fa_fwd_pair_kernel): B1 H8 N8192 causal, inputs x3: 295
-        // against 367 us for one wavefront per 32 rows at the same tile.
+        // The kernel split by role (fa_fwd_role_kernel), 32-key blocks: B1 H8 N8192
+        // causal, inputs x3: 282-293 against 289-303 us for the wavefront pairs at
+        // 128 x 64 (interleaved, four boxes), which had replaced one wavefront per
+        // 32 rows (367 us).
         br = 128;
-        bc = 64;
+        bc = 32;
     } else if (d == 128) {
         // 256 x 64 from N = 4096 (causal) or N = 2048 (no mask), 128 x 64 below
         // (causal N = 2048: 51.4 against 53.9 us for 128 x 32; no mask, N = 1024:

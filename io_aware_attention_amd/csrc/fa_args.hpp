@@ -36,6 +36,14 @@ constexpr int fwd_pair_lds_bytes()
     return 2 * fwd_stage_bytes(256, 64) + 4 * 4 * 64 * 16 + 2 * 4 * 2 * 32 * 4 + 2 * 4 * 4;
 }
 
+// LDS bytes of the head-dim-256 kernel split by role: a ring of three stages of
+// 32-key blocks, P^T operands of four groups in two buffers (16 KB), their rescale
+// factors and flags, and the final row sums.
+constexpr int fwd_role_lds_bytes()
+{
+    return 3 * fwd_stage_bytes(256, 32) + 2 * 4 * 2 * 64 * 16 + 2 * 4 * 32 * 4 + 2 * 4 * 4 + 4 * 32 * 4;
+}
+
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
@@ -92,6 +100,10 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 // query rows (fa_fwd_pair_kernel.hpp).
 template <typename T, bool CAUSAL, bool OUT_F32>
 hipError_t launch_fwd_pair(const FwdArgs &a, hipStream_t stream);
+// Head dim 256, 128 x 32 tiles, eight wavefronts split by role: a score and an
+// output wavefront per 32 query rows (fa_fwd_role_kernel.hpp).
+template <typename T, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd_role(const FwdArgs &a, hipStream_t stream);
 
 // Forward with an additive bias on the scaled scores.
 template <typename T, int D, int BC, int WAVES, bool CAUSAL>
@@ -138,15 +150,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
     X(T, D, 64, 8, true, false)  X(T, D, 64, 8, true, true)                           \
     X(T, D, 64, 2, false, false) X(T, D, 64, 2, true, false)
 
-// Head dim 256, one wavefront per 32 rows: tile 128 x 32, also with fp32 output.
-// (The 128 x 64 tile is the wavefront-pair kernel below.)
-#define FA355_VARIANTS_D256(X, T)                                                     \
-    X(T, 256, 32, 4, false, false) X(T, 256, 32, 4, false, true)                      \
-    X(T, 256, 32, 4, true, false)  X(T, 256, 32, 4, true, true)
-
-// Head dim 256 with wavefront pairs: P(T, CAUSAL, OUT_F32).
-#define FA355_PAIR_VARIANTS(P, T)                                                     \
+// Head dim 256 (four variants each: P(T, CAUSAL, OUT_F32)): the kernel split by
+// role at tile 128 x 32 (the default), and the wavefront pairs at 128 x 64.
+#define FA355_ROLE_VARIANTS(P, T)                                                     \
     P(T, false, false) P(T, false, true) P(T, true, false) P(T, true, true)
+#define FA355_PAIR_VARIANTS(P, T) FA355_ROLE_VARIANTS(P, T)
 
 #define FA355_VARIANTS_F32(Y) Y(1, false) Y(1, true) Y(2, false) Y(2, true) Y(4, false) Y(4, true)
 

@@ -3,6 +3,7 @@
 
 #include "fa_fwd_kernel.hpp"
 #include "fa_fwd_pair_kernel.hpp"
+#include "fa_fwd_role_kernel.hpp"
 
 namespace fa355 {
 
@@ -52,6 +53,15 @@ hipError_t launch_fwd_pair(const FwdArgs &a, hipStream_t stream)
     return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(PairTraits::NT), params, 0, stream);   // static LDS
 }
 
+template <typename T, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd_role(const FwdArgs &a, hipStream_t stream)
+{
+    const void *fn = reinterpret_cast<const void *>(&fa_fwd_role_kernel<T, CAUSAL, OUT_F32>);
+    FwdArgs arg = a;
+    void *params[] = {&arg};
+    return hipLaunchKernel(fn, dim3(a.total_tiles), dim3(RoleTraits::NT), params, 0, stream);   // static LDS
+}
+
 template <int WAVES, bool CAUSAL>
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
 {
@@ -68,6 +78,8 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream)
     template hipError_t fa355::launch_fwd<fa355::T, D, BC, W, C, O>(const fa355::FwdArgs &, hipStream_t);
 #define FA355_INSTANTIATE_PAIR(T, C, O)                                               \
     template hipError_t fa355::launch_fwd_pair<fa355::T, C, O>(const fa355::FwdArgs &, hipStream_t);
+#define FA355_INSTANTIATE_ROLE(T, C, O)                                               \
+    template hipError_t fa355::launch_fwd_role<fa355::T, C, O>(const fa355::FwdArgs &, hipStream_t);
 #define FA355_INSTANTIATE_F32(W, C)                                                   \
     template hipError_t fa355::launch_fwd_f32<W, C>(const fa355::FwdArgs &, hipStream_t);
 #define FA355_INSTANTIATE_SPLIT(T, D, BC, W, C)                                       \

@@ -66,14 +66,18 @@ def test_valid_call_plans_a_launch():
     rc, p = check(B_=1, Hq=1, Hkv=1, N=128, d=64, dt=F.F32, tuning=(32, 32))
     assert rc == 0 and (p.br, p.bc, p.grid) == (32, 32, 4)
     rc, p = check(d=256, N=8192, Hq=8, Hkv=8)
-    assert rc == 0 and (p.br, p.bc) == (128, 64)
-    # Head dim 256: eight wavefronts in pairs; two stages, the pairs' P operands
-    # (16 KB), block maxima and row sums (2 x 1 KB), rescale flags (32 B).
+    assert rc == 0 and (p.br, p.bc) == (128, 32)
+    # Head dim 256 by default: eight wavefronts split by role; three stages of 32-key
+    # blocks, P operands of four groups in two buffers (16 KB), rescale factors
+    # (1 KB) and flags (32 B), final row sums (512 B).
     ceil64 = lambda n: (n + 63) // 64 * 64
+    stage32 = 16 * (ceil64(32 * 33) + 32 * 32)
+    assert p.waves == 8 and p.lds_bytes == 3 * stage32 + 16384 + 1024 + 32 + 512 == 119328
+    # The wavefront pairs at 128 x 64: two stages, the pairs' P operands (16 KB),
+    # block maxima and row sums (2 x 1 KB), rescale flags (32 B).
+    rc, p = check(d=256, N=8192, Hq=8, Hkv=8, tuning=(128, 64))
     stage = 16 * (ceil64(64 * 33) + 64 * 32)
-    assert p.waves == 8 and p.lds_bytes == 2 * stage + 16384 + 2048 + 32 == 151584
-    rc, p = check(d=256, N=8192, Hq=8, Hkv=8, tuning=(128, 32))
-    assert rc == 0 and p.waves == 4
+    assert rc == 0 and p.waves == 8 and p.lds_bytes == 2 * stage + 16384 + 2048 + 32 == 151584
     # d = 64: fp16 takes 128 x 32 for short rows, 256 x 64 without a mask from 2048 and
     # 128 x 64 with one from 4096; bf16 takes 256 x 64, except causal rows below 2048.
     f16 = lambda N, c: (check(d=64, N=N, dt=F.F16, causal=c)[1].br, check(d=64, N=N, dt=F.F16, causal=c)[1].bc)

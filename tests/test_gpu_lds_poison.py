@@ -58,7 +58,8 @@ FWD = [
     # (B, Hq, Hkv, N, d, dtype, causal, tilings)
     (1, 4, 2, 300, 128, "bf16", True, [None, (128, 32), (64, 64), (256, 64), (128, 64)]),
     (2, 3, 3, 77, 64, "f16", False, [None, (128, 32), (64, 64), (256, 64)]),
-    (1, 2, 1, 200, 256, "bf16", True, [None, (128, 32)]),
+    (1, 2, 1, 200, 256, "bf16", True, [None, (128, 64)]),
+    (1, 2, 2, 300, 256, "f16", False, [None, (128, 64)]),
     (1, 2, 2, 129, 256, "f16", False, [None]),
     (1, 2, 2, 100, 64, "f32", True, [None, (32, 32), (64, 32), (128, 32)]),
     (1, 1, 1, 1, 128, "bf16", True, [None]),

@@ -2,7 +2,7 @@
 
 A head's K, V (and Q, O) must fit 32-bit byte offsets: N d 2 <= INT_MAX - 65536 for
 16-bit inputs, i.e. N <= 8,388,351 at d = 128 and 4,194,175 at d = 256 (the
-wavefront-pair kernel), each with a ragged last tile.  Inputs
+kernel split by role), each with a ragged last tile.  Inputs
 of that size are built on the device, and the expected result comes from integer
 counting rather than from the oracle:
 

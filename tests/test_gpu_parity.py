@@ -303,14 +303,17 @@ def test_empty_inputs():
                False, "after empty calls")
 
 
+@pytest.mark.parametrize("tl", [None, (128, 64)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-def test_growing_row_maximum_d256_pairs(dt, causal):
-    # Head dim 256 (wavefront pairs, 128 x 64 tiles): keys growing along the
-    # sequence drive the rescale path mid-row, and the query rows of one pair
-    # (rows 32..63 of each tile) are scaled up 4x, so in many blocks that pair's
-    # wavefronts go over the cap while the other pairs of the workgroup do not --
-    # the rescale is then taken by some pairs only, with every pair at the barriers.
+def test_growing_row_maximum_d256_groups(dt, causal, tl):
+    # Head dim 256 (default: score and output wavefronts per 32-row group, 128 x 32
+    # tiles; (128, 64): wavefront pairs): keys growing along the sequence drive the
+    # rescale path mid-row, and query rows 32..63 of each tile are scaled up 4x, so
+    # in many blocks that group's weights go over the cap while the other groups of
+    # the workgroup do not -- the rescale (and, split by role, the hand-over of its
+    # factors) is then taken by some groups only, with every wavefront at the
+    # barriers.
     x = G.make_inputs(9450, 1, 2, 2, 700, 256, dt, causal)
     ramp = 1.0 + np.arange(x.N) / 96.0
     k = G.to_storage(G.round_to_dtype(x.f64("k") * ramp[:, None], dt), dt)
@@ -319,8 +322,8 @@ def test_growing_row_maximum_d256_pairs(dt, causal):
     q = G.to_storage(G.round_to_dtype(x.f64("q") * qs[:, None], dt), dt)
     x = G.AttentionInputs(x.B, x.Hq, x.Hkv, x.N, x.d, dt, causal, x.scale, x.seed, q, k, x.v)
     o_ref, l_ref = full_oracle(x)
-    o, l = run_gpu(x)
-    PT.compare(o, l, o_ref, l_ref, dt, False, f"{dt} d256 pairs growing max causal={causal}")
+    o, l = run_gpu(x, tuning=tl)
+    PT.compare(o, l, o_ref, l_ref, dt, False, f"{dt} d256 growing max causal={causal} tile={tl}")
 
 
 @pytest.mark.parametrize("tl", [None, (128, 32), (64, 64), (256, 64)])

@@ -6,7 +6,7 @@
 * The forward pass and the decoding pair of kernels are captured into HIP graphs
   (through torch.cuda.CUDAGraph) and replayed several times, with eager work and
   synchronisations between the replays; every replay reproduces the eager result
-  bit for bit.  The same holds for the head-dim-256 forward (wavefront pairs), the
+  bit for bit.  The same holds for the head-dim-256 forward (split by role), the
   no-allocation decoding entry point (the caller graph capture is for) and the
   backward pass.  No library kernel needs a memset, so nothing the capture records
   depends on one.
@@ -121,7 +121,7 @@ def test_graph_capture_and_replay():
                "bf16", False, "graph replay")
 
 
-def test_graph_capture_pairs_noalloc_backward():
+def test_graph_capture_d256_noalloc_backward():
     x = G.make_inputs(9980, 1, 4, 2, 333, 256, "bf16", True)
     q, k, v = PT.to_device(x)
     dx, dq, dk, dv = _decode_inputs(9981)
