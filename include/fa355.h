@@ -107,7 +107,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *             (identical arithmetic; only the final store differs)
  *   tuning    NULL or {0,0} for the default tiles, else one of the built tilings
  *             (br, bc): for F16/BF16 with d = 64 or 128, (128,64), (128,32), (256,64)
- *             (also with F32 output) and (64,64); with d = 256, (128,64), (128,32);
+ *             (also with F32 output) and (64,64); with d = 256, (128,32) (the
+ *             default: a score and an output wavefront per 32 query rows) and
+ *             (128,64) (wavefront pairs), each also with F32 output;
  *             for F32, (32,32), (64,32), (128,32)
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
